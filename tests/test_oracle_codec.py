@@ -1,0 +1,149 @@
+"""Pins of the oracle's K and V codecs and of the code-group packing.
+
+PolyKV explainer, section 2.B: K to int8 under a per-tensor linear scale;
+V by FWHT rotation, Lloyd-Max N(0, 1) codes and dequantisation by centroid
+lookup plus inverse FWHT.  CoMixKV news article: 2/3/4-bit V per layer.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import codec, hadamard, lloyd_max
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- K
+def test_k_worked_example_scale_one():
+    # amax = 127 gives scale exactly 1, so codes are rint(k) with ties to even
+    k = np.array([127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -127.0, 0.49], dtype=np.float32)
+    s, q = codec.k_quantize(k)
+    assert s == np.float32(1.0)
+    assert q.tolist() == [127, 2, 4, -2, 0, 0, 2, -127, 0]
+
+
+def test_k_worked_example_scale_two():
+    k = np.array([254.0, 5.0, 7.0, -3.0], dtype=np.float32)  # s = 2: 2.5 -> 2, 3.5 -> 4, -1.5 -> -2
+    s, q = codec.k_quantize(k)
+    assert s == np.float32(2.0) and q.tolist() == [127, 2, 4, -2]
+
+
+def test_k_bounds_symmetry_and_error():
+    rng = np.random.default_rng(4)
+    k = (rng.standard_normal((8, 300, 128)) * rng.lognormal(0, 0.5, 128)).astype(np.float32)
+    s, q = codec.k_quantize(k)
+    amax = np.max(np.abs(k))
+    assert s == np.float32(amax / np.float32(127.0))
+    assert q.dtype == np.int8 and q.min() >= -127 and q.max() <= 127
+    i = np.unravel_index(np.argmax(np.abs(k)), k.shape)
+    assert abs(int(q[i])) == 127
+    err = np.abs(k.astype(np.float64) - float(s) * q.astype(np.float64))
+    assert np.all(err <= 0.5 * float(s) * (1 + 1e-6) + 1e-30)
+    s2, q2 = codec.k_quantize(-k)
+    assert s2 == s and np.array_equal(q2, -q)
+
+
+def test_k_zero_tensor():
+    s, q = codec.k_quantize(np.zeros((2, 3, 64), dtype=np.float32))
+    assert s == 0.0 and not q.any()
+
+
+# ---------------------------------------------------------------- V
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_codes_are_nearest_centroid(bits, d):
+    # Lloyd-Max thresholds are centroid midpoints, so the threshold count equals the
+    # nearest centroid of the rotated, normalised coordinate (computed here in fp64)
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((400, d)).astype(np.float32)
+    n, codes = codec.v_encode(v, bits)
+    y = hadamard.fwht_f32(v).astype(np.float64) / n.astype(np.float64)[:, None]
+    c, _ = lloyd_max.table_f32(bits)
+    near = np.argmin(np.abs(y[..., None] - c.astype(np.float64)), axis=-1)
+    # fp32 y differs from fp64 y by ~1e-7; allow mismatches only within that of a threshold
+    _, t = lloyd_max.table_f32(bits)
+    close = np.min(np.abs(y[..., None] - t.astype(np.float64)), axis=-1) < 1e-5
+    assert np.all((codes == near) | close)
+    assert np.mean(codes == near) > 0.999
+
+
+def test_v_tie_goes_to_lower_code():
+    # a coordinate exactly on a threshold takes the lower code (strict comparison)
+    d, bits = 64, 3
+    _, thr = lloyd_max.table_f32(bits)
+    v = np.zeros((1, d), dtype=np.float32)
+    v[0, 0] = 1.0  # H e_0 = all ones; n = 1 -> y_i = 1 for every i
+    n, codes = codec.v_encode(v, bits)
+    assert n[0] == 1.0
+    expected = int(np.sum(np.float32(1.0) > thr))
+    assert np.all(codes == expected)
+    v2 = np.zeros((1, d), dtype=np.float32)
+    v2[0, 0] = 1.0
+    v2[0, 1] = 1.0  # H(e0 + e1): entries 2 or 0; n = sqrt(2); y = 0 on half the coords
+    _, c2 = codec.v_encode(v2, bits)
+    z = hadamard.fwht_f32(v2)[0]
+    assert np.all(c2[0][z == 0] == 3)  # y = 0 equals tau_3 = 0: not greater, so code 3 (of 0..7)
+
+
+def test_v_zero_vector():
+    n, codes = codec.v_encode(np.zeros((3, 128), dtype=np.float32), 3)
+    assert not n.any() and not codes.any()
+    assert not codec.v_decode(n, codes, 3).any()
+
+
+@pytest.mark.parametrize("bits,lo,hi", [(2, 0.9, 1.0), (3, 0.9, 1.0), (4, 0.9, 1.0)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_relative_mse_band(bits, d, lo, hi):
+    # ||v - v_hat||^2 / ||v||^2 = ||y - c||^2 / d: the per-coordinate Lloyd-Max distortion
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal((2000, d)) * rng.lognormal(0, 0.5, d)).astype(np.float32)
+    n, codes = codec.v_encode(v, bits)
+    vh = codec.v_decode(n, codes, bits)
+    rel = np.mean(np.sum((v - vh) ** 2, axis=1) / np.sum(v.astype(np.float64) ** 2, axis=1))
+    c, t = lloyd_max.lloyd_max_normal(bits)
+    dmse = lloyd_max.mse_closed_form(c, t)
+    assert lo * dmse <= rel <= hi * dmse
+
+
+def test_v_decode_is_inverse_transform_of_centroids():
+    # v_hat = (n/d) H c: applying the fp32 FWHT to v_hat recovers n * c exactly enough
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((10, 64)).astype(np.float32)
+    n, codes = codec.v_encode(v, 3)
+    vh = codec.v_decode(n, codes, 3)
+    c, _ = lloyd_max.table_f32(3)
+    back = vh @ hadamard.hadamard_matrix(64).astype(np.float64)
+    assert np.allclose(back, n[:, None] * c.astype(np.float64)[codes], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_worked_examples():
+    ex = json.load(open(os.path.join(GOLD, "pack_examples.json")))
+    for case in ex["cases"]:
+        b = case["bits"]
+        codes = np.zeros((8, 64), dtype=np.uint8)
+        codes[:, 0] = case["codes"]
+        packed = codec.pack_group(codes, b)
+        assert packed.size == 64 * b
+        assert packed[:b].tobytes().hex() == case["bytes_hex"]
+        assert not packed[b:].any()
+        # the same field placed at dimension 5 lands at bytes [5b, 6b)
+        codes2 = np.zeros((8, 64), dtype=np.uint8)
+        codes2[:, 5] = case["codes"]
+        p2 = codec.pack_group(codes2, b)
+        assert p2[5 * b:6 * b].tobytes().hex() == case["bytes_hex"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_pack_roundtrip_and_vectorised_agrees(bits, d):
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 2 ** bits, size=(3, 40, d)).astype(np.uint8)
+    packed = codec.pack_codes(codes, bits)
+    assert packed.shape == (3, 5, d * bits)
+    assert np.array_equal(codec.unpack_codes(packed, d, bits), codes)
+    for a in range(3):
+        for g in range(5):
+            assert np.array_equal(packed[a, g], codec.pack_group(codes[a, 8 * g:8 * g + 8], bits))
