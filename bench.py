@@ -1,0 +1,218 @@
+"""Benchmark of the shared compressed-KV decode path on one MI355X.
+
+One step is the whole hot path of the Llama-3-8B-shaped workload (32 layers,
+32 q heads / 8 kv heads, head_dim 128, a 4096-token shared context, 15 agents):
+the pool is encoded from bf16 K/V already resident in HBM (one append of all
+layers), then 128 decode steps run for all 15 agents, each agent attending to
+the pool plus its own native bf16 suffix of s + 1 tokens at decode step s.
+value = agent-tokens per second = 15 * 128 / (seconds per step).
+
+The JSON line also carries the roofline of the dominant kernel (the pool
+decode kernel), timed live with a HIP event pair recorded on the call's own
+stream around the kernel, and the CPU oracle timed on a bounded sample of the
+same work.  Only the ``cpu_baseline`` leg imports the oracle.
+
+    python bench.py [--steps K] [--warmup W] [--kernel valu|mfma|default] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--kernel", default="default", choices=["default", "valu", "mfma"])
+    ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per job (default: workload's 128)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                            "pool_decode_traffic.json"))
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as wl
+    from quantized_shared_kv_amd import polykv as pk
+
+    pk.lib()  # fails loudly if the HIP library is not built
+    kernel = {"default": pk.KERNEL_DEFAULT, "valu": pk.KERNEL_VALU, "mfma": pk.KERNEL_MFMA}[args.kernel]
+    w = wl.LLAMA3_8B
+    steps_per_job = args.decode_steps or w.steps
+    dev = "cuda:0"
+    L, Hkv, Hq, d, T, A, S = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens, w.n_agents, w.sfx_tokens
+
+    def dev_bf16(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+
+    t0 = time.time()
+    log("[bench] generating inputs")
+    k_pool = torch.empty((L, Hkv, T, d), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty_like(k_pool)
+    for l in range(L):
+        k_pool[l].copy_(dev_bf16(w.pool_k(0, l).raw))
+        v_pool[l].copy_(dev_bf16(w.pool_v(0, l).raw))
+    sfx_k = torch.empty((A, L, Hkv, S, d), dtype=torch.bfloat16, device=dev)
+    sfx_v = torch.empty_like(sfx_k)
+    for a in range(A):
+        for l in range(L):
+            sfx_k[a, l].copy_(dev_bf16(w.sfx_k(a, l).raw))
+            sfx_v[a, l].copy_(dev_bf16(w.sfx_v(a, l).raw))
+    q_all = torch.empty((steps_per_job, A, L, Hq, d), dtype=torch.bfloat16, device=dev)
+    for s in range(steps_per_job):
+        for a in range(A):
+            q_all[s, a].copy_(dev_bf16(w.queries(s, a).raw))
+    out = torch.empty((A, L, Hq, d), dtype=torch.float32, device=dev)
+    cfg = pk.make_config(L, Hkv, d, T, w.v_bits(0))
+    nbytes = pk.pool_bytes(cfg)
+    pool_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = pk.pool_build(cfg, pool_buf.data_ptr(), nbytes)
+    pools = [pool] * A
+    ws_bytes = pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A, kernel=kernel)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in {time.time() - t0:.1f}s; pool {nbytes / 1e6:.1f} MB, workspace "
+        f"{ws_bytes / 1e6:.1f} MB")
+
+    n_ev = steps_per_job
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for e0, e1 in evs:  # create the underlying events
+        e0.record()
+        e1.record()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def one_job(timed_kernels):
+        pool_fresh = pk.pool_build(cfg, pool_buf.data_ptr(), nbytes)  # host-only: n_tokens back to 0
+        for f in pk.Pool._fields_:
+            setattr(pool, f[0], getattr(pool_fresh, f[0]))
+        if timed_kernels:
+            b0.record()
+        pk.pool_quantize_append(pool, 0, k_pool, v_pool)
+        if timed_kernels:
+            b1.record()
+        for s in range(steps_per_job):
+            lens = [min(s + 1, S)] * A
+            pk.agent_decode_attention(pools, q_all[s], out, 0, sfx_k, sfx_v, lens, workspace=ws, kernel=kernel,
+                                      pool_events=evs[s] if timed_kernels else None)
+
+    for i in range(args.warmup):
+        one_job(False)
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pool_ms, build_ms = [], []
+    start.record()
+    for i in range(args.steps):
+        one_job(True)
+        torch.cuda.synchronize()  # event readback between jobs; inside the timed region
+        pool_ms += [e0.elapsed_time(e1) for e0, e1 in evs]
+        build_ms.append(b0.elapsed_time(b1))
+        log(f"[bench] step {i + 1}/{args.steps} done")
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    value = A * steps_per_job / (ms_per_step / 1e3)
+
+    # algorithmic bytes of one pool-kernel launch: every pool byte of the T tokens once
+    # (K codes d, V codes d*b/8, norm 4 per (token, kv head); scale 4 per (token, layer)) + bf16 queries
+    bits = 3
+    pool_alg = L * Hkv * T * (d + d * bits // 8 + 4) + L * T * 4
+    q_bytes = A * L * Hq * d * 2
+    alg = pool_alg + q_bytes
+    avg_pool_ms = float(np.mean(pool_ms))
+    achieved = alg / (avg_pool_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            t = json.load(open(args.traffic_json))
+            if t.get("kernel_variant") == args.kernel and t.get("workload") == w.name:
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    line = {
+        "metric": "compressed-KV decode attention: achieved HBM GB/s (% peak) + agent-tokens/s",
+        "value": value,
+        "unit": "agent-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if kernel == pk.KERNEL_VALU else "f32-acc",
+        "data": "synthetic",
+        "config": {"workload": w.name, "agents": A, "decode_steps_per_step": steps_per_job, "pool_tokens": T,
+                   "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "v_bits": 3,
+                   "suffix": f"bf16, s+1 tokens at decode step s (max {S})", "kernel": args.kernel},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "pool decode", "alg_bytes_per_launch": alg, "avg_launch_us": avg_pool_ms * 1e3},
+        "pool_build_us": float(np.mean(build_ms)) * 1e3,
+        "decode_step_us": (ms_per_step - float(np.mean(build_ms))) / steps_per_job * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, steps_per_job)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, steps_per_job):
+    """The oracle, untuned, on a bounded sample of the same job, scaled to agent-tokens/s.
+
+    Sample: layers 0-1 of the pool build (oracle codec on the same bf16 values)
+    and one decode step over those layers for all agents (fp64 oracle attention).
+    Job time = L/2 * (build of 2 layers + steps_per_job * decode of 2 layers).
+    """
+    from oracle import attention, pool_image
+
+    threads = len(os.sched_getaffinity(0))
+    L, T = w.n_layers, w.pool_tokens
+    nl = 2
+    t0 = time.perf_counter()
+    img = pool_image.PoolImage(nl, w.n_kv_heads, w.head_dim, T, w.v_bits(0)[:nl])
+    img.append(0, np.stack([w.pool_k(0, l).f32 for l in range(nl)]), np.stack([w.pool_v(0, l).f32 for l in range(nl)]))
+    t_build = time.perf_counter() - t0
+    q = np.stack([w.queries(0, a).f32[:nl] for a in range(w.n_agents)])
+    sk = [[w.sfx_k(a, l).f32 for l in range(nl)] for a in range(w.n_agents)]
+    sv = [[w.sfx_v(a, l).f32 for l in range(nl)] for a in range(w.n_agents)]
+    cache = {}
+
+    def decoded(p, l, g):
+        if (l, g) not in cache:
+            cache[(l, g)] = img.decoded_layer(l, g)
+        return cache[(l, g)]
+
+    t1 = time.perf_counter()
+    attention.decode_call(q, [0] * w.n_agents, decoded, lambda a, l: sk[a][l], lambda a, l: sv[a][l],
+                          [1] * w.n_agents, w.n_kv_heads)
+    t_dec = time.perf_counter() - t1
+    job = (L / nl) * (t_build + steps_per_job * t_dec)
+    return {"value": w.n_agents * steps_per_job / job, "unit": "agent-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"layers 0-{nl - 1}: pool build ({t_build:.2f}s) + 1 decode step for {w.n_agents} agents "
+                      f"({t_dec:.2f}s), scaled x{L // nl} layers and x{steps_per_job} decode steps",
+            "sample_seconds": t_build + t_dec}
+
+
+if __name__ == "__main__":
+    main()

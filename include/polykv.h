@@ -1,0 +1,210 @@
+/*
+ * polykv.h - C ABI of the shared, asymmetrically compressed KV pool and of
+ * fused multi-agent decode attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * What the pool is (PolyKV explainer, section 2.A "core architecture"):
+ * the KV state of a shared context is computed once, compressed, and stored
+ * as one object that many agents read; its memory does not grow with the
+ * number of agents.  How it is compressed (section 2.B "asymmetric
+ * compression scheme"): K becomes int8 under a per-tensor linear scale; V is
+ * rotated by a fast Walsh-Hadamard transform, normalised, and each
+ * coordinate is replaced by the index of its Lloyd-Max cell for N(0, 1).
+ * CoMixKV (news article: abstract and "incremental quantization strategy")
+ * chooses the V bit width per (agent, layer) among 2, 3 and 4, keeps the most
+ * recent tokens at native precision, and never re-quantises stored blocks.
+ *
+ * Conventions shared by every entry point:
+ *  - Return value: PKV_OK (0) or a negative PKV_E* code.  All validation is
+ *    done on the host, synchronously, before anything is enqueued; on error
+ *    nothing is enqueued and no output is modified.
+ *  - Device memory is always owned by the caller.  The library allocates
+ *    neither device nor pinned host memory and keeps no global state except
+ *    immutable constant tables.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every device effect is enqueued on it, asynchronously.  Calls that touch
+ *    the same pool must be ordered on one stream by the caller; calls on
+ *    distinct pools and workspaces may run concurrently.
+ *  - Inputs holding NaN or Inf give undefined (but memory-safe) results.
+ */
+#ifndef POLYKV_H
+#define POLYKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_MAX_LAYERS 128
+
+enum {
+    PKV_OK = 0,
+    PKV_EINVAL = -1,        /* null pointer, bad shape or count, inconsistent arguments */
+    PKV_EUNSUPPORTED = -2,  /* head_dim not 64/128, bits not 2/3/4, unknown dtype */
+    PKV_ECAPACITY = -3,     /* append would exceed the pool's token capacity */
+    PKV_ENOSPACE = -4,      /* device buffer or workspace smaller than required */
+    PKV_EHIP = -5           /* a kernel launch failed (hipGetLastError) */
+};
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Shape of one pool.  K always uses 8 bits; V uses v_bits[l] bits in layer l. */
+typedef struct {
+    int32_t n_layers;                /* 1 .. PKV_MAX_LAYERS */
+    int32_t n_kv_heads;              /* >= 1 */
+    int32_t head_dim;                /* 64 or 128 */
+    int32_t capacity_tokens;         /* >= 1; rounded up to a multiple of 32 internally */
+    uint8_t v_bits[PKV_MAX_LAYERS];  /* 2, 3 or 4 for layers 0 .. n_layers-1 */
+} pkv_pool_config;
+
+/*
+ * Descriptor of one pool: a plain struct in caller-owned host memory (no
+ * destroy call).  It records where each region lives inside the caller's
+ * device buffer and how many tokens each layer holds.  The byte layout, each
+ * region starting on a 256-byte boundary, with tc = capacity rounded up to 32:
+ *
+ *   Kq    int8 [L][Hkv][tc][d]            K codes (two's complement, -127..127)
+ *   Vn    f32  [L][Hkv][tc]               V norms ||v|| (plain L2 norm)
+ *   Ks    f32  [L][tc]                    K scale of the append block holding each token
+ *   Vmax  f32  [L][Hkv]                   max V norm over the tokens stored so far
+ *   Vc    u8   per layer l: [Hkv][tc/8][d * v_bits[l]]   packed V code groups
+ *   amax  u32  [L]                        scratch used by pool_quantize_append
+ *
+ * A V code group covers 8 consecutive tokens of one (layer, kv head): for
+ * each dimension i = 0 .. d-1 in order, one little-endian field of
+ * 8 * bits bits holding the codes of the 8 tokens, token j in bits
+ * [bits*j, bits*(j+1)) (at 3 bits: 8 codes in 3 bytes).  Codes index the
+ * Lloyd-Max centroids in ascending order.  Bits of tokens not yet stored are 0.
+ */
+typedef struct {
+    pkv_pool_config cfg;
+    void* base;                          /* device buffer (caller-owned) */
+    uint64_t bytes;                      /* bytes of the buffer in use (= pool_bytes(cfg)) */
+    int32_t tc;                          /* capacity rounded up to 32 */
+    int32_t n_tokens[PKV_MAX_LAYERS];    /* tokens stored per layer; advanced by appends */
+    uint64_t off_kq, off_vn, off_ks, off_vmax, off_amax;
+    uint64_t off_vc[PKV_MAX_LAYERS + 1]; /* off_vc[l] .. off_vc[l+1]: codes of layer l */
+} pkv_pool;
+
+/*
+ * Bytes of device memory one pool of this shape needs (the layout above).
+ * The value does not depend on how many agents will read the pool (PolyKV
+ * explainer, section 4 "memory efficiency": pool size is constant in the agent
+ * count).  Returns 0 if cfg is NULL or invalid.
+ */
+size_t pool_bytes(const pkv_pool_config* cfg);
+
+/*
+ * Lay a pool out in a caller-owned device buffer.  Host-only: writes the
+ * descriptor *out (offsets, tc, n_tokens = 0) and enqueues no device work.
+ * dev_buf must be 256-byte aligned and dev_bytes >= pool_bytes(cfg).
+ * Errors: PKV_EINVAL (NULL, misaligned), PKV_EUNSUPPORTED (head_dim, bits),
+ * PKV_ENOSPACE (dev_bytes too small).
+ */
+int pool_build(const pkv_pool_config* cfg, void* dev_buf, size_t dev_bytes, pkv_pool* out);
+
+/*
+ * Quantise n_tokens new tokens into layers [layer_begin, layer_begin +
+ * layer_count) of the pool (PolyKV explainer, section 2.B; CoMixKV article,
+ * "incremental quantization strategy": new tokens are appended, earlier
+ * tokens are never re-quantised).
+ *
+ *   k, v   device [layer_count][n_kv_heads][n_tokens][head_dim], dtype
+ *          PKV_F32 or PKV_BF16, contiguous; read only.
+ *
+ * Per layer, the K values of this call form one tensor with one scale:
+ * s = amax / 127 (amax = max |k| over all heads, tokens and channels of that
+ * layer in this call), codes = clamp(rint(k / s), -127, 127), or s = 0 and
+ * codes 0 when amax = 0.  Each V vector x gets n = ||x|| (squares summed by a
+ * halving tree, correctly rounded sqrt), z = H x (unnormalised Sylvester
+ * Hadamard, butterflies with ascending half-width), y = z * (1/n), and
+ * code_i = number of Lloyd-Max N(0, 1) thresholds strictly below y_i; n = 0
+ * gives codes 0.  All of it is fp32 without contraction, so codes are
+ * reproducible bit for bit.
+ *
+ * All layers in the range must hold the same number of tokens before the
+ * call.  On success pool->n_tokens[l] is advanced on the host at enqueue time.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED (dtype), PKV_ECAPACITY, PKV_EHIP.
+ */
+int pool_quantize_append(pkv_pool* pool, int32_t layer_begin, int32_t layer_count,
+                         const void* k, const void* v, pkv_dtype dtype, int32_t n_tokens,
+                         void* stream);
+
+/* Arguments of one multi-agent decode-attention call. */
+typedef struct {
+    int32_t n_agents;                 /* >= 0; 0 is a no-op */
+    int32_t n_q_heads;                /* multiple of the pools' n_kv_heads */
+    int32_t layer_begin;              /* first pool layer attended */
+    int32_t layer_count;              /* layers in this call (>= 0) */
+    float softmax_scale;              /* 0 => 1 / sqrt(head_dim) */
+    const pkv_pool* const* agent_pool;/* host [n_agents]; agents with the same pointer share a pool */
+    const void* q;                    /* device [n_agents][layer_count][n_q_heads][head_dim] */
+    pkv_dtype q_dtype;                /* PKV_F32 or PKV_BF16 */
+    const void* sfx_k;                /* device [n_agents][layer_count][n_kv_heads][sfx_cap][head_dim] */
+    const void* sfx_v;                /* same shape; both may be NULL when every sfx_len is 0 */
+    pkv_dtype sfx_dtype;              /* PKV_F32 or PKV_BF16 */
+    int32_t sfx_cap;                  /* suffix capacity per agent (>= max sfx_len) */
+    const int32_t* sfx_len;           /* host [n_agents]: native tokens agent a attends to; may be NULL (all 0) */
+    float* out;                       /* device fp32 [n_agents][layer_count][n_q_heads][head_dim] */
+    int32_t kernel;                   /* 0 = default, PKV_KERNEL_VALU, PKV_KERNEL_MFMA */
+    int32_t splits;                   /* token splits per (pool, layer, kv head); 0 = automatic */
+    void* const* pool_events;         /* optional instrumentation: NULL, or two hipEvent_t recorded on
+                                         the stream right before the first and right after the last
+                                         pool-kernel launch of the call */
+} pkv_decode_args;
+
+#define PKV_KERNEL_DEFAULT 0
+#define PKV_KERNEL_VALU 1
+#define PKV_KERNEL_MFMA 2
+
+/*
+ * Decode attention of every agent's query heads over its pool plus its own
+ * native (uncompressed) recent tokens, for layers [layer_begin, layer_begin
+ * + layer_count).  PolyKV explainer, section 2.A: agents read one shared
+ * pool; section 2.B: V is dequantised by centroid lookup and inverse FWHT.
+ *
+ * For agent a, layer l, query head h (kv head g = h / (n_q_heads/n_kv_heads)):
+ *   o = softmax(sigma * q . [K_hat; K_sfx]) @ [V_hat; V_sfx]
+ * with K_hat = Ks * Kq and V_hat = (Vn / d) * H @ c[code] over the pool's
+ * tokens, and the first sfx_len[a] suffix tokens; no mask.  Each pool byte is
+ * read once per call for all agents that share the pool (their query heads
+ * are batched), V is accumulated in the rotated domain and one inverse FWHT
+ * is applied per output.  fp32 accumulation.
+ *
+ * workspace: device scratch of *workspace_bytes bytes (256-byte aligned).
+ * Call with workspace == NULL to have the required size written to
+ * *workspace_bytes (nothing enqueued); PKV_ENOSPACE if the given size is too
+ * small.  The size depends only on the call's shapes and the split plan.
+ * All agents' pools must share n_kv_heads and head_dim, hold the layers of the
+ * call, and hold the same token count in each of those layers.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOSPACE, PKV_EHIP.
+ */
+int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
+                           void* stream);
+
+/* ---- auxiliary queries (host only, no device work) ---- */
+
+/* Static text for a return code. */
+const char* pkv_strerror(int code);
+
+/* ABI version: 100 * major + minor. */
+int pkv_version(void);
+
+/* sizeof of the ABI structs, for bindings to check their mirrors:
+ * which = 0: pkv_pool_config, 1: pkv_pool, 2: pkv_decode_args; else 0. */
+size_t pkv_abi_sizeof(int32_t which);
+
+/*
+ * The library's fp32 Lloyd-Max N(0, 1) table for `bits` in {2, 3, 4}
+ * (PolyKV explainer, section 2.B): centroids[2^bits] ascending and
+ * thresholds[2^bits - 1] (midpoints, computed in double, then rounded).
+ * Either pointer may be NULL.  Returns PKV_EUNSUPPORTED for other bits.
+ */
+int pkv_lloyd_max_table(int32_t bits, float* centroids, float* thresholds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POLYKV_H */

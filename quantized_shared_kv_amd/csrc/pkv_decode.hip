@@ -1,0 +1,552 @@
+// Decode attention of many agents over shared compressed pools (gfx950).
+//
+// PolyKV explainer, section 2.A: agents hold a reference to one shared pool
+// and attend over it; section 2.B: V is dequantised by centroid lookup and an
+// inverse FWHT.  CoMixKV news article: the most recent tokens of each agent
+// stay at native precision.  Here the pool is never dequantised into memory:
+// the kernels read the compressed bytes, form scores from int8 K times the
+// per-token scale, and accumulate p * norm * centroid in the rotated domain;
+// the merge kernel applies one inverse FWHT per output row.
+//
+// Launch sequence of one call (all on the caller's stream):
+//   1. k_sfx_valu    per (agent, layer, kv head): partial softmax state over
+//                    the agent's native suffix tokens (unrotated domain)
+//   2. pool kernel   per (pool, layer, kv head, token split): partial state of
+//                    all rows that read the pool (every agent of the pool times
+//                    every q head of the kv head's group), rotated domain;
+//                    k_pool_valu here or the MFMA kernel in pkv_decode_mfma.hip
+//   3. k_merge       per output row: combine splits, inverse FWHT, add suffix
+// Softmax state is kept in log2 units: scores are scaled by sigma * log2(e).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "pkv_decode.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kValuRows = 32;  // rows per VALU workgroup
+constexpr int kTile = 32;      // tokens per tile
+constexpr int kThreads = 256;
+
+struct Centroids {
+    float c[3][16];
+};
+
+__device__ __forceinline__ float ld_elem(const void* p, int dtype, uint64_t i) {
+    if (dtype == PKV_BF16) {
+        const uint16_t b = static_cast<const uint16_t*>(p)[i];
+        return __uint_as_float(static_cast<uint32_t>(b) << 16);
+    }
+    return static_cast<const float*>(p)[i];
+}
+
+template <int D>
+struct ValuSmem {
+    float q[kValuRows][D];
+    float k[kTile][D + 1];
+    float v[kTile][D + 1];
+    float sc[kValuRows][kTile + 1];
+    float f[kTile];
+    float nn[kTile];
+    float m[kValuRows], l[kValuRows], al[kValuRows];
+    int valid[kTile];
+};
+
+// Online softmax over tokens [t_begin, t_end) for nr rows whose queries are in sm.q.
+// acc[k] holds element idx = tid + 256 k of the row-major [nr][D] accumulator.
+template <int D, class Src>
+__device__ void valu_attend(ValuSmem<D>& sm, int nr, int t_begin, int t_end, const Src& src,
+                            float* acc) {
+    constexpr int ACC = kValuRows * D / kThreads;
+    const int tid = threadIdx.x;
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+        src.load_tile(sm, t0, t_end);
+        __syncthreads();
+        for (int pair = tid; pair < nr * kTile; pair += kThreads) {
+            const int r = pair / kTile, t = pair % kTile;
+            float dot = 0.0f;
+#pragma unroll 8
+            for (int i = 0; i < D; ++i) dot += sm.q[r][i] * sm.k[t][i];
+            sm.sc[r][t] = sm.valid[t] ? dot * sm.f[t] : -INFINITY;
+        }
+        __syncthreads();
+        if (tid < nr) {
+            const float mold = sm.m[tid];
+            float mx = mold;
+            for (int t = 0; t < kTile; ++t) mx = fmaxf(mx, sm.sc[tid][t]);
+            const float alpha = (mold == -INFINITY) ? 0.0f : exp2f(mold - mx);
+            float sum = 0.0f;
+            for (int t = 0; t < kTile; ++t) {
+                const float s = sm.sc[tid][t];
+                const float p = (s == -INFINITY) ? 0.0f : exp2f(s - mx);
+                sum += p;
+                sm.sc[tid][t] = p * sm.nn[t];
+            }
+            sm.l[tid] = sm.l[tid] * alpha + sum;
+            sm.m[tid] = mx;
+            sm.al[tid] = alpha;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < ACC; ++k) {
+            const int idx = tid + kThreads * k;
+            const int r = idx / D, i = idx % D;
+            if (r < nr) {
+                float v = acc[k] * sm.al[r];
+                for (int t = 0; t < kTile; ++t) v += sm.sc[r][t] * sm.v[t][i];
+                acc[k] = v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Token source reading a compressed pool: int8 K * scale, V centroids * norm.
+template <int D>
+struct PoolSrc {
+    const int8_t* kq;
+    const float* vn;
+    const float* ks;
+    const uint8_t* vc;
+    const float* cent;
+    int bits;
+    float sm_log2;
+    __device__ void load_tile(ValuSmem<D>& sm, int t0, int t_end) const {
+        const int tid = threadIdx.x;
+        for (int idx = tid; idx < kTile * D; idx += kThreads) {
+            const int t = idx / D, i = idx % D;
+            const int tok = t0 + t;
+            sm.k[t][i] = tok < t_end ? static_cast<float>(kq[(uint64_t)tok * D + i]) : 0.0f;
+        }
+        const uint32_t mask = (1u << bits) - 1u;
+        for (int idx = tid; idx < 4 * D; idx += kThreads) {
+            const int gi = idx / D, dim = idx % D;
+            const uint8_t* fp = vc + ((uint64_t)(t0 / kGroupTokens + gi) * D + dim) * bits;
+            uint32_t field = 0;
+            for (int b = 0; b < bits; ++b) field |= static_cast<uint32_t>(fp[b]) << (8 * b);
+            for (int i = 0; i < kGroupTokens; ++i) sm.v[gi * kGroupTokens + i][dim] = cent[(field >> (bits * i)) & mask];
+        }
+        if (tid < kTile) {
+            const int tok = t0 + tid;
+            const bool ok = tok < t_end;
+            sm.valid[tid] = ok;
+            sm.f[tid] = ok ? ks[tok] * sm_log2 : 0.0f;
+            sm.nn[tid] = ok ? vn[tok] : 0.0f;
+        }
+    }
+};
+
+// Token source reading an agent's native suffix K/V rows.
+template <int D>
+struct SfxSrc {
+    const void* k;
+    const void* v;
+    int dtype;
+    uint64_t base;  // element offset of token 0
+    float sm_log2;
+    __device__ void load_tile(ValuSmem<D>& sm, int t0, int t_end) const {
+        const int tid = threadIdx.x;
+        for (int idx = tid; idx < kTile * D; idx += kThreads) {
+            const int t = idx / D, i = idx % D;
+            const int tok = t0 + t;
+            const bool ok = tok < t_end;
+            sm.k[t][i] = ok ? ld_elem(k, dtype, base + (uint64_t)tok * D + i) : 0.0f;
+            sm.v[t][i] = ok ? ld_elem(v, dtype, base + (uint64_t)tok * D + i) : 0.0f;
+        }
+        if (tid < kTile) {
+            const bool ok = t0 + tid < t_end;
+            sm.valid[tid] = ok;
+            sm.f[tid] = sm_log2;
+            sm.nn[tid] = ok ? 1.0f : 0.0f;
+        }
+    }
+};
+
+template <int D>
+__device__ void load_rows_and_init(ValuSmem<D>& sm, const DecodeLaunch& a, int nr, int lj,
+                                   const int* agents, const int* heads, float* acc) {
+    const int tid = threadIdx.x;
+    for (int idx = tid; idx < kValuRows * D; idx += kThreads) {
+        const int r = idx / D, i = idx % D;
+        float x = 0.0f;
+        if (r < nr) x = ld_elem(a.q, a.q_dtype, (((uint64_t)agents[r] * a.lc + lj) * a.hq + heads[r]) * D + i);
+        sm.q[r][i] = x;
+    }
+    if (tid < kValuRows) {
+        sm.m[tid] = -INFINITY;
+        sm.l[tid] = 0.0f;
+    }
+    constexpr int ACC = kValuRows * D / kThreads;
+#pragma unroll
+    for (int k = 0; k < ACC; ++k) acc[k] = 0.0f;
+    __syncthreads();
+}
+
+template <int D>
+__device__ void store_records(const ValuSmem<D>& sm, int nr, float* const* recs, const float* acc) {
+    constexpr int ACC = kValuRows * D / kThreads;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < ACC; ++k) {
+        const int idx = tid + kThreads * k;
+        const int r = idx / D, i = idx % D;
+        if (r < nr) recs[r][2 + i] = acc[k];
+    }
+    if (tid < nr) {
+        recs[tid][0] = sm.m[tid];
+        recs[tid][1] = sm.l[tid];
+    }
+}
+
+__device__ __forceinline__ int find_pool(const DecodeLaunch& a, int wg) {
+    int p = 0;
+    while (p + 1 < a.n_pools && wg >= a.pools[p + 1].wg_begin) ++p;
+    return p;
+}
+
+// grid: one workgroup per (pool, layer, kv head, split, row block of 32 rows)
+template <int D>
+__global__ void __launch_bounds__(kThreads) k_pool_valu(DecodeLaunch a, Centroids cents) {
+    __shared__ ValuSmem<D> sm;
+    __shared__ int agents[kValuRows], heads[kValuRows];
+    __shared__ float* recs[kValuRows];
+    const int p = find_pool(a, blockIdx.x);
+    const PoolEntry& P = a.pools[p];
+    int local = blockIdx.x - P.wg_begin;
+    const int rb = local % P.rblocks;
+    local /= P.rblocks;
+    const int s = local % P.splits;
+    local /= P.splits;
+    const int g = local % a.hkv;
+    const int lj = local / a.hkv;
+    const int l = a.l0 + lj;
+    const int r0 = rb * kValuRows;
+    const int nr = min(kValuRows, P.rows - r0);
+    if (threadIdx.x < kValuRows) {
+        const int rho = min(r0 + (int)threadIdx.x, P.rows - 1);
+        agents[threadIdx.x] = a.agent_id[P.agent0 + rho / a.G];
+        heads[threadIdx.x] = g * a.G + rho % a.G;
+        recs[threadIdx.x] = a.part + P.part_off +
+                            ((((uint64_t)lj * a.hkv + g) * P.splits + s) * P.rows + rho) * (2 + D);
+    }
+    __syncthreads();
+    float acc[kValuRows * D / kThreads];
+    load_rows_and_init(sm, a, nr, lj, agents, heads, acc);
+
+    const int bits = layer_bits(P, l);
+    PoolSrc<D> src;
+    src.kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
+    src.vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
+    src.ks = reinterpret_cast<const float*>(P.base + P.off_ks) + (uint64_t)l * P.tc;
+    src.vc = P.base + P.off_vc0 + (uint64_t)a.hkv * P.tc * (D / 8) * layer_bits_prefix(P, l) +
+             (uint64_t)g * (P.tc / kGroupTokens) * D * bits;
+    src.cent = cents.c[bits - 2];
+    src.bits = bits;
+    src.sm_log2 = a.sm_log2;
+    const int tb = s * P.chunk;
+    const int te = min(P.T, tb + P.chunk);
+    valu_attend<D>(sm, nr, tb, te, src, acc);
+    store_records<D>(sm, nr, recs, acc);
+}
+
+// grid (lc * hkv, n_agents): one workgroup per (agent, layer, kv head); rows = the G heads
+template <int D>
+__global__ void __launch_bounds__(kThreads) k_sfx_valu(DecodeLaunch a) {
+    __shared__ ValuSmem<D> sm;
+    __shared__ int agents[kValuRows], heads[kValuRows];
+    __shared__ float* recs[kValuRows];
+    const int k = blockIdx.y;
+    const int lj = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+    const int agent = a.agent_id[k];
+    const int S = a.sfx_len[k];
+    for (int r0 = 0; r0 < a.G; r0 += kValuRows) {
+        const int nr = min(kValuRows, a.G - r0);
+        if (threadIdx.x < kValuRows) {
+            const int h = g * a.G + min(r0 + (int)threadIdx.x, a.G - 1);
+            agents[threadIdx.x] = agent;
+            heads[threadIdx.x] = h;
+            recs[threadIdx.x] = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + h) * (2 + D);
+        }
+        __syncthreads();
+        float acc[kValuRows * D / kThreads];
+        load_rows_and_init(sm, a, nr, lj, agents, heads, acc);
+        SfxSrc<D> src;
+        src.k = a.sfx_k;
+        src.v = a.sfx_v;
+        src.dtype = a.sfx_dtype;
+        src.base = (((uint64_t)agent * a.lc + lj) * a.hkv + g) * (uint64_t)a.sfx_cap * D;
+        src.sm_log2 = a.sm_log2;
+        valu_attend<D>(sm, nr, 0, S, src, acc);
+        store_records<D>(sm, nr, recs, acc);
+        __syncthreads();
+    }
+}
+
+// One wavefront per output row (launch agent, layer, q head): combine the
+// pool's split records, apply the inverse FWHT (H / d) to the rotated-domain
+// accumulator, fold in the suffix record and normalise.
+template <int D>
+__global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
+    constexpr int EPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint64_t n_rows = (uint64_t)a.n_agents * a.lc * a.hq;
+    if (row >= n_rows) return;
+    const int h = row % a.hq;
+    const int lj = (row / a.hq) % a.lc;
+    const int k = row / ((uint64_t)a.hq * a.lc);
+    const PoolEntry& P = a.pools[a.agent_pool[k]];
+    const int g = h / a.G;
+    const int rho = a.agent_pos[k] * a.G + h % a.G;
+    const float* rec0 = a.part + P.part_off + ((((uint64_t)lj * a.hkv + g) * P.splits) * P.rows + rho) * (2 + D);
+    const uint64_t stride = (uint64_t)P.rows * (2 + D);
+    float M = -INFINITY;
+    for (int s = 0; s < P.splits; ++s) M = fmaxf(M, rec0[s * stride]);
+    float L = 0.0f, z[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < P.splits; ++s) {
+            const float* r = rec0 + s * stride;
+            const float w = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
+            L += w * r[1];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) z[e] += w * r[2 + EPL * lane + e];
+        }
+    }
+    // inverse transform: H z / D (lane holds dims EPL*lane + e)
+    if (EPL == 2) {
+        const float u = z[0], w = z[EPL - 1];
+        z[0] = u + w;
+        z[EPL - 1] = u - w;
+    }
+#pragma unroll
+    for (int off = 1; off <= 32; off <<= 1) {
+        const bool upper = (lane & off) != 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float pz = __shfl_xor(z[e], off, 64);
+            z[e] = upper ? (pz - z[e]) : (z[e] + pz);
+        }
+    }
+    const float inv_d = 1.0f / D;
+    float o[EPL];
+    float denom;
+    if (a.has_sfx) {
+        const float* ru = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + h) * (2 + D);
+        const float mu = ru[0];
+        const float M2 = fmaxf(M, mu);
+        const float ap = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
+        const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
+        denom = ap * L + au * ru[1];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = ap * z[e] * inv_d + au * ru[2 + EPL * lane + e];
+    } else {
+        denom = L;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = z[e] * inv_d;
+    }
+    const float rl = denom > 0.0f ? 1.0f / denom : 0.0f;
+    float* out = a.out + (((uint64_t)a.agent_id[k] * a.lc + lj) * a.hq + h) * D + EPL * lane;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = o[e] * rl;
+}
+
+// ------------------------------------------------------------------ host plan
+struct Plan {
+    std::vector<DecodeLaunch> launches;
+    std::vector<int> pool_wg;  // workgroups of the pool kernel per launch
+    size_t ws_floats = 0;
+};
+
+int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
+    const pkv_pool* p0 = x->agent_pool[0];
+    const int hkv = p0->cfg.n_kv_heads, d = p0->cfg.head_dim;
+    const int G = x->n_q_heads / hkv;
+    const float sigma = x->softmax_scale != 0.0f ? x->softmax_scale : 1.0f / std::sqrt((float)d);
+
+    // group agents by pool (first appearance order)
+    std::vector<const pkv_pool*> order;
+    std::map<const pkv_pool*, std::vector<int>> members;
+    for (int a = 0; a < x->n_agents; ++a) {
+        const pkv_pool* p = x->agent_pool[a];
+        if (!members.count(p)) order.push_back(p);
+        members[p].push_back(a);
+    }
+    // pool chunks of at most kMaxAgentsPerLaunch agents
+    struct Chunk { const pkv_pool* pool; std::vector<int> agents; };
+    std::vector<Chunk> chunks;
+    for (const pkv_pool* p : order) {
+        const std::vector<int>& m = members[p];
+        for (size_t i = 0; i < m.size(); i += kMaxAgentsPerLaunch)
+            chunks.push_back({p, std::vector<int>(m.begin() + i, m.begin() + std::min(m.size(), i + kMaxAgentsPerLaunch))});
+    }
+    size_t ci = 0;
+    while (ci < chunks.size()) {
+        DecodeLaunch L;
+        std::memset(&L, 0, sizeof(L));
+        L.q = x->q;
+        L.sfx_k = x->sfx_k;
+        L.sfx_v = x->sfx_v;
+        L.out = x->out;
+        L.q_dtype = x->q_dtype;
+        L.sfx_dtype = x->sfx_dtype;
+        L.hq = x->n_q_heads;
+        L.hkv = hkv;
+        L.G = G;
+        L.d = d;
+        L.l0 = x->layer_begin;
+        L.lc = x->layer_count;
+        L.sfx_cap = x->sfx_cap;
+        L.sm_log2 = sigma * 1.4426950408889634f;
+        int n_agents = 0, wg = 0;
+        uint64_t part = 0;
+        while (ci < chunks.size() && L.n_pools < kMaxPoolsPerLaunch &&
+               n_agents + (int)chunks[ci].agents.size() <= kMaxAgentsPerLaunch) {
+            const Chunk& c = chunks[ci];
+            PoolEntry& e = L.pools[L.n_pools];
+            const pkv_pool* p = c.pool;
+            e.base = static_cast<const uint8_t*>(p->base);
+            e.off_kq = p->off_kq;
+            e.off_vn = p->off_vn;
+            e.off_ks = p->off_ks;
+            e.off_vmax = p->off_vmax;
+            e.off_vc0 = p->off_vc[0];
+            for (int l = 0; l < p->cfg.n_layers; ++l) {
+                if (p->cfg.v_bits[l] >= 3) e.ge3[l >> 5] |= 1u << (l & 31);
+                if (p->cfg.v_bits[l] == 4) e.eq4[l >> 5] |= 1u << (l & 31);
+            }
+            e.T = p->n_tokens[x->layer_begin];
+            e.tc = p->tc;
+            e.rows = (int)c.agents.size() * G;
+            e.agent0 = n_agents;
+            const int units = x->layer_count * hkv;
+            const int tiles = std::max(1, (e.T + kTile - 1) / kTile);
+            int splits = x->splits;
+            if (splits <= 0) splits = std::max(1, std::min(tiles, (2 * 256 + units - 1) / units));
+            splits = std::min(splits, tiles);
+            e.chunk = (tiles + splits - 1) / splits * kTile;
+            e.splits = std::max(1, (std::max(e.T, 1) + e.chunk - 1) / e.chunk);
+            e.rblocks = use_mfma ? 1 : (e.rows + kValuRows - 1) / kValuRows;
+            e.wg_begin = wg;
+            e.part_off = part;
+            part += (uint64_t)units * e.splits * e.rows * record_floats(d);
+            wg += units * e.splits * e.rblocks;
+            for (size_t i = 0; i < c.agents.size(); ++i) {
+                const int a = c.agents[i];
+                L.agent_id[n_agents] = (int16_t)a;
+                L.agent_pool[n_agents] = (int16_t)L.n_pools;
+                L.agent_pos[n_agents] = (int16_t)i;
+                const int s = x->sfx_len ? x->sfx_len[a] : 0;
+                L.sfx_len[n_agents] = s;
+                if (s > 0) L.has_sfx = 1;
+                ++n_agents;
+            }
+            ++L.n_pools;
+            ++ci;
+        }
+        L.n_agents = n_agents;
+        if (L.has_sfx) {
+            L.sfx_part_off = part;
+            part += (uint64_t)n_agents * x->layer_count * x->n_q_heads * record_floats(d);
+        }
+        plan->ws_floats = std::max<size_t>(plan->ws_floats, part);
+        plan->launches.push_back(L);
+        plan->pool_wg.push_back(wg);
+    }
+    return PKV_OK;
+}
+
+int validate(const pkv_decode_args* x) {
+    if (!x) return PKV_EINVAL;
+    if (x->n_agents < 0 || x->layer_count < 0 || x->layer_begin < 0 || x->n_q_heads < 1) return PKV_EINVAL;
+    if (x->n_agents == 0 || x->layer_count == 0) return PKV_OK;
+    if (x->n_agents > 32767) return PKV_EINVAL;
+    if (!x->agent_pool || !x->q || !x->out) return PKV_EINVAL;
+    if (x->q_dtype != PKV_F32 && x->q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+    if (x->kernel < 0 || x->kernel > PKV_KERNEL_MFMA || x->splits < 0) return PKV_EINVAL;
+    if (!(x->softmax_scale >= 0.0f) || std::isinf(x->softmax_scale)) return PKV_EINVAL;
+    const pkv_pool* p0 = x->agent_pool[0];
+    if (!p0) return PKV_EINVAL;
+    for (int a = 0; a < x->n_agents; ++a) {
+        const pkv_pool* p = x->agent_pool[a];
+        if (!p || !p->base) return PKV_EINVAL;
+        int err;
+        if (!config_valid(&p->cfg, &err)) return err;
+        if (p->cfg.n_kv_heads != p0->cfg.n_kv_heads || p->cfg.head_dim != p0->cfg.head_dim) return PKV_EINVAL;
+        if (x->layer_begin + x->layer_count > p->cfg.n_layers) return PKV_EINVAL;
+        const int T = p->n_tokens[x->layer_begin];
+        for (int l = x->layer_begin; l < x->layer_begin + x->layer_count; ++l)
+            if (p->n_tokens[l] != T) return PKV_EINVAL;
+        if (T < 0 || T > p->cfg.capacity_tokens) return PKV_EINVAL;
+    }
+    if (x->n_q_heads % p0->cfg.n_kv_heads) return PKV_EINVAL;
+    bool any_sfx = false;
+    for (int a = 0; a < x->n_agents; ++a) {
+        const int s = x->sfx_len ? x->sfx_len[a] : 0;
+        if (s < 0 || s > x->sfx_cap) return PKV_EINVAL;
+        any_sfx |= s > 0;
+    }
+    if (any_sfx) {
+        if (!x->sfx_k || !x->sfx_v) return PKV_EINVAL;
+        if (x->sfx_dtype != PKV_F32 && x->sfx_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+    }
+    return PKV_OK;
+}
+
+template <int D>
+int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hipStream_t s) {
+    Centroids cents;
+    std::memcpy(cents.c, codebook_tables().cent, sizeof(cents.c));
+    for (size_t i = 0; i < plan.launches.size(); ++i) {
+        DecodeLaunch L = plan.launches[i];
+        L.part = ws;
+        if (L.has_sfx)
+            hipLaunchKernelGGL(k_sfx_valu<D>, dim3(L.lc * L.hkv, L.n_agents), dim3(kThreads), 0, s, L);
+        if (events && i == 0) hipEventRecord(static_cast<hipEvent_t>(events[0]), s);
+        if (use_mfma) {
+            const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
+            if (st != PKV_OK) return st;
+        } else {
+            hipLaunchKernelGGL(k_pool_valu<D>, dim3(plan.pool_wg[i]), dim3(kThreads), 0, s, L, cents);
+        }
+        if (events && i + 1 == plan.launches.size()) hipEventRecord(static_cast<hipEvent_t>(events[1]), s);
+        const uint64_t rows = (uint64_t)L.n_agents * L.lc * L.hq;
+        hipLaunchKernelGGL(k_merge<D>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, L);
+    }
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
+                                      void* stream) {
+    using namespace pkv;
+    if (!workspace_bytes) return PKV_EINVAL;
+    const int v = validate(args);
+    if (v != PKV_OK) return v;
+    if (args->n_agents == 0 || args->layer_count == 0) {
+        if (!workspace) *workspace_bytes = 0;
+        return PKV_OK;
+    }
+    bool use_mfma = false;
+    Plan plan;
+    make_plan(args, use_mfma, &plan);
+    const size_t need = plan.ws_floats * sizeof(float);
+    if (!workspace) {
+        *workspace_bytes = need;
+        return PKV_OK;
+    }
+    if (*workspace_bytes < need) return PKV_ENOSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return PKV_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    if (args->pool_events && (!args->pool_events[0] || !args->pool_events[1])) return PKV_EINVAL;
+    if (args->agent_pool[0]->cfg.head_dim == 128) return enqueue<128>(plan, use_mfma, ws, args->pool_events, s);
+    return enqueue<64>(plan, use_mfma, ws, args->pool_events, s);
+}

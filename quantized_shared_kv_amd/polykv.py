@@ -1,0 +1,196 @@
+"""ctypes binding of libpolykv (include/polykv.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it turns torch tensors into device pointers and
+dtype codes, checks shapes the C side cannot see, calls the library and raises
+``PolyKVError`` on a non-zero return.  There is no fallback: if the built
+library is missing, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_void_p
+
+MAX_LAYERS = 128
+PKV_F32, PKV_BF16 = 0, 1
+KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
+          -5: "PKV_EHIP"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libpolykv.so")
+
+
+class PolyKVError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERRORS.get(code, code)} ({lib().pkv_strerror(code).decode()})")
+
+
+class PoolConfig(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
+                ("capacity_tokens", c_int32), ("v_bits", c_uint8 * MAX_LAYERS)]
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("cfg", PoolConfig), ("base", c_void_p), ("bytes", c_uint64), ("tc", c_int32),
+                ("n_tokens", c_int32 * MAX_LAYERS), ("off_kq", c_uint64), ("off_vn", c_uint64),
+                ("off_ks", c_uint64), ("off_vmax", c_uint64), ("off_amax", c_uint64),
+                ("off_vc", c_uint64 * (MAX_LAYERS + 1))]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("n_agents", c_int32), ("n_q_heads", c_int32), ("layer_begin", c_int32),
+                ("layer_count", c_int32), ("softmax_scale", c_float),
+                ("agent_pool", POINTER(POINTER(Pool))), ("q", c_void_p), ("q_dtype", c_int32),
+                ("sfx_k", c_void_p), ("sfx_v", c_void_p), ("sfx_dtype", c_int32), ("sfx_cap", c_int32),
+                ("sfx_len", POINTER(c_int32)), ("out", c_void_p), ("kernel", c_int32), ("splits", c_int32),
+                ("pool_events", POINTER(c_void_p))]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built: run python -m quantized_shared_kv_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pool_bytes.argtypes = [POINTER(PoolConfig)]
+        L.pool_bytes.restype = c_size_t
+        L.pool_build.argtypes = [POINTER(PoolConfig), c_void_p, c_size_t, POINTER(Pool)]
+        L.pool_build.restype = c_int32
+        L.pool_quantize_append.argtypes = [POINTER(Pool), c_int32, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                           c_void_p]
+        L.pool_quantize_append.restype = c_int32
+        L.agent_decode_attention.argtypes = [POINTER(DecodeArgs), c_void_p, POINTER(c_size_t), c_void_p]
+        L.agent_decode_attention.restype = c_int32
+        L.pkv_strerror.argtypes = [c_int32]
+        L.pkv_strerror.restype = ctypes.c_char_p
+        L.pkv_version.restype = c_int32
+        L.pkv_abi_sizeof.argtypes = [c_int32]
+        L.pkv_abi_sizeof.restype = c_size_t
+        L.pkv_lloyd_max_table.argtypes = [c_int32, POINTER(c_float), POINTER(c_float)]
+        L.pkv_lloyd_max_table.restype = c_int32
+        for i, s in enumerate((PoolConfig, Pool, DecodeArgs)):
+            if L.pkv_abi_sizeof(i) != ctypes.sizeof(s):
+                raise ImportError(f"ABI mismatch for {s.__name__}")
+        _LIB = L
+    return _LIB
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise PolyKVError(rc, where)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def make_config(n_layers: int, n_kv_heads: int, head_dim: int, capacity_tokens: int, v_bits) -> PoolConfig:
+    cfg = PoolConfig(n_layers, n_kv_heads, head_dim, capacity_tokens)
+    vb = list(v_bits) if hasattr(v_bits, "__len__") else [int(v_bits)] * n_layers
+    for i, b in enumerate(vb):
+        cfg.v_bits[i] = int(b)
+    return cfg
+
+
+def pool_bytes(cfg: PoolConfig) -> int:
+    return int(lib().pool_bytes(ctypes.byref(cfg)))
+
+
+def pool_build(cfg: PoolConfig, dev_ptr: int, dev_bytes: int) -> Pool:
+    pool = Pool()
+    _check(lib().pool_build(ctypes.byref(cfg), c_void_p(dev_ptr), dev_bytes, ctypes.byref(pool)), "pool_build")
+    return pool
+
+
+def pool_quantize_append(pool: Pool, layer_begin: int, k, v, stream=None) -> None:
+    """k, v: device tensors [layer_count][n_kv_heads][n_tokens][head_dim], fp32 or bf16."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+        raise ValueError("k and v must be equal-shape 4-D tensors")
+    if not (k.is_contiguous() and v.is_contiguous()) or not k.is_cuda:
+        raise ValueError("k and v must be contiguous device tensors")
+    nl, hkv, n, d = k.shape
+    if hkv != pool.cfg.n_kv_heads or d != pool.cfg.head_dim:
+        raise ValueError("k/v shape does not match the pool")
+    _check(lib().pool_quantize_append(ctypes.byref(pool), layer_begin, nl, c_void_p(k.data_ptr()),
+                                      c_void_p(v.data_ptr()), _dtype_code(k), n, c_void_p(_stream_handle(stream))),
+           "pool_quantize_append")
+
+
+def _decode_args(pools, q, out, layer_begin, sfx_k=None, sfx_v=None, sfx_len=None, softmax_scale=0.0,
+                 kernel=KERNEL_DEFAULT, splits=0, pool_events=None):
+    n_agents = len(pools)
+    arr = (POINTER(Pool) * max(n_agents, 1))(*[ctypes.pointer(p) for p in pools])
+    lens = (c_int32 * max(n_agents, 1))(*(list(sfx_len) if sfx_len is not None else [0] * n_agents))
+    A, lc, hq, d = q.shape
+    if A != n_agents or tuple(out.shape) != (A, lc, hq, d) or not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q/out must be contiguous [n_agents][layers][n_q_heads][head_dim]")
+    a = DecodeArgs()
+    a.n_agents, a.n_q_heads, a.layer_begin, a.layer_count = n_agents, hq, layer_begin, lc
+    a.softmax_scale = softmax_scale
+    a.agent_pool = arr
+    a.q = q.data_ptr()
+    a.q_dtype = _dtype_code(q)
+    a.out = out.data_ptr()
+    if sfx_k is not None:
+        if sfx_k.shape != sfx_v.shape or sfx_k.dim() != 5 or not sfx_k.is_contiguous() or not sfx_v.is_contiguous():
+            raise ValueError("sfx_k/sfx_v must be contiguous [n_agents][layers][n_kv_heads][sfx_cap][head_dim]")
+        a.sfx_k, a.sfx_v = sfx_k.data_ptr(), sfx_v.data_ptr()
+        a.sfx_dtype = _dtype_code(sfx_k)
+        a.sfx_cap = sfx_k.shape[3]
+    a.sfx_len = lens
+    a.kernel, a.splits = kernel, splits
+    evs = None
+    if pool_events is not None:
+        evs = (c_void_p * 2)(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in pool_events])
+        a.pool_events = ctypes.cast(evs, POINTER(c_void_p))
+    return a, (arr, lens, evs)
+
+
+def agent_decode_attention(pools, q, out, layer_begin=0, sfx_k=None, sfx_v=None, sfx_len=None, workspace=None,
+                           softmax_scale=0.0, kernel=KERNEL_DEFAULT, splits=0, stream=None,
+                           pool_events=None) -> int:
+    """Enqueue one decode call.  pools: list of Pool (one per agent; the same object = shared pool).
+
+    With workspace=None only the required workspace size is computed and returned.
+    pool_events: optional pair of recorded torch.cuda.Event (or raw hipEvent_t handles)
+    bracketing the pool kernel.  Returns the workspace bytes the call needs.
+    """
+    a, keep = _decode_args(pools, q, out, layer_begin, sfx_k, sfx_v, sfx_len, softmax_scale, kernel, splits,
+                           pool_events)
+    size = c_size_t(0)
+    if workspace is None:
+        _check(lib().agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None), "agent_decode_attention")
+        return int(size.value)
+    size.value = workspace.numel() * workspace.element_size()
+    _check(lib().agent_decode_attention(ctypes.byref(a), c_void_p(workspace.data_ptr()), ctypes.byref(size),
+                                        c_void_p(_stream_handle(stream))), "agent_decode_attention")
+    del keep
+    return int(size.value)
+
+
+def lloyd_max_table(bits: int):
+    """The library's fp32 (centroids, thresholds) lists for `bits`."""
+    c = (c_float * 16)()
+    t = (c_float * 15)()
+    _check(lib().pkv_lloyd_max_table(bits, c, t), "pkv_lloyd_max_table")
+    return list(c[: 1 << bits]), list(t[: (1 << bits) - 1])

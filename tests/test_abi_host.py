@@ -1,0 +1,191 @@
+"""Host-side checks of the C ABI (no GPU): symbols, struct mirrors, layout, tables, errors.
+
+Nothing here enqueues device work: every call either is host-only
+(pool_bytes, pool_build, the auxiliary queries, a workspace-size query) or
+fails host-side validation before any launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import lloyd_max, pool_image
+from quantized_shared_kv_amd import polykv as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "polykv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"pool_bytes", "pool_build", "pool_quantize_append", "agent_decode_attention"}
+    lib = pk.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_mirrors_match_c_sizes():
+    lib = pk.lib()
+    assert lib.pkv_abi_sizeof(0) == ctypes.sizeof(pk.PoolConfig)
+    assert lib.pkv_abi_sizeof(1) == ctypes.sizeof(pk.Pool)
+    assert lib.pkv_abi_sizeof(2) == ctypes.sizeof(pk.DecodeArgs)
+    assert lib.pkv_abi_sizeof(3) == 0
+    assert lib.pkv_version() == 100
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64, 512, [3]), (24, 32, 64, 1851, [3] * 24), (32, 8, 128, 4096, [3] * 32),
+                                   (32, 8, 128, 7194, [3] * 32), (3, 2, 128, 33, [2, 4, 3]), (5, 3, 64, 1, [4] * 5)])
+def test_layout_matches_oracle(shape):
+    L, H, d, cap, bits = shape
+    cfg = pk.make_config(L, H, d, cap, bits)
+    ref = pool_image.layout(L, H, d, cap, bits)
+    assert pk.pool_bytes(cfg) == ref.total
+    pool = pk.pool_build(cfg, 256 * 1024, ref.total)  # a fake aligned address: host-only
+    assert pool.tc == ref.tc and pool.bytes == ref.total
+    assert (pool.off_kq, pool.off_vn, pool.off_ks, pool.off_vmax, pool.off_amax) == (ref.kq, ref.vn, ref.ks, ref.vmax,
+                                                                                       ref.amax)
+    assert list(pool.off_vc[:L + 1]) == ref.vc
+    assert list(pool.n_tokens[:L]) == [0] * L
+
+
+def test_pool_bytes_has_no_agent_dimension():
+    # the only inputs are the pool shape: the same bytes serve any number of agents
+    cfg = pk.make_config(32, 8, 128, 4096, 3)
+    n = pk.pool_bytes(cfg)
+    assert n == pool_image.layout(32, 8, 128, 4096, [3] * 32).total
+    # 180 bytes per (token, kv head) plus one 4-byte scale per (token, layer), plus padding
+    assert 0 <= n - (32 * 8 * 4096 * 180 + 32 * 4096 * 4 + 32 * 8 * 4) < 5 * 256 + 32 * 4 + 256
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_library_table_equals_oracle_table_bitwise(bits):
+    # two independent solvers (C++ erfc, NumPy/SciPy ndtr) of the same fixed point
+    c, t = pk.lloyd_max_table(bits)
+    rc, rt = lloyd_max.table_f32(bits)
+    assert np.array_equal(np.array(c, dtype=np.float32).view(np.uint32), rc.view(np.uint32))
+    assert np.array_equal(np.array(t, dtype=np.float32).view(np.uint32), rt.view(np.uint32))
+
+
+def test_lloyd_table_rejects_other_bits():
+    with pytest.raises(pk.PolyKVError):
+        pk.lloyd_max_table(5)
+
+
+def test_config_errors():
+    lib = pk.lib()
+    assert lib.pool_bytes(None) == 0
+    bad = [pk.make_config(0, 1, 64, 10, []), pk.make_config(1, 0, 64, 10, [3]), pk.make_config(1, 1, 96, 10, [3]),
+           pk.make_config(1, 1, 64, 0, [3]), pk.make_config(2, 1, 64, 10, [3, 5]), pk.make_config(1, 1, 64, 10, [1])]
+    for cfg in bad:
+        assert pk.pool_bytes(cfg) == 0
+    good = pk.make_config(2, 1, 64, 10, [3, 2])
+    n = pk.pool_bytes(good)
+    out = pk.Pool()
+    assert lib.pool_build(ctypes.byref(good), ctypes.c_void_p(4096), n - 1, ctypes.byref(out)) == -4
+    assert lib.pool_build(ctypes.byref(good), ctypes.c_void_p(4096 + 16), n, ctypes.byref(out)) == -1
+    assert lib.pool_build(ctypes.byref(good), None, n, ctypes.byref(out)) == -1
+    assert lib.pool_build(ctypes.byref(good), ctypes.c_void_p(4096), n, None) == -1
+    assert lib.pool_build(ctypes.byref(bad[2]), ctypes.c_void_p(4096), n, ctypes.byref(out)) == -2
+
+
+def _fake_pool(L=2, H=2, d=64, cap=100, bits=3):
+    cfg = pk.make_config(L, H, d, cap, bits)
+    return pk.pool_build(cfg, 1 << 20, pk.pool_bytes(cfg))
+
+
+def test_quantize_append_validation_errors():
+    lib = pk.lib()
+    pool = _fake_pool()
+    f = lib.pool_quantize_append
+    k = ctypes.c_void_p(1 << 24)
+    assert f(None, 0, 1, k, k, 0, 4, None) == -1
+    assert f(ctypes.byref(pool), 0, 3, k, k, 0, 4, None) == -1           # layers out of range
+    assert f(ctypes.byref(pool), -1, 1, k, k, 0, 4, None) == -1
+    assert f(ctypes.byref(pool), 0, 1, k, k, 7, 4, None) == -2           # dtype
+    assert f(ctypes.byref(pool), 0, 1, None, k, 0, 4, None) == -1
+    assert f(ctypes.byref(pool), 0, 1, ctypes.c_void_p((1 << 24) + 4), k, 0, 4, None) == -1  # misaligned
+    assert f(ctypes.byref(pool), 0, 1, k, k, 0, 101, None) == -3         # capacity
+    assert f(ctypes.byref(pool), 0, 1, k, k, 0, -1, None) == -1
+    assert f(ctypes.byref(pool), 0, 0, k, k, 0, 4, None) == 0            # empty: no-op
+    assert f(ctypes.byref(pool), 0, 1, k, k, 0, 0, None) == 0
+    pool.n_tokens[0] = 8                                                  # unequal layer counts
+    assert f(ctypes.byref(pool), 0, 2, k, k, 0, 4, None) == -1
+    assert list(pool.n_tokens[:2]) == [8, 0]
+
+
+class _FakeT:
+    """Minimal stand-in with the attributes the binding reads, for host-only calls."""
+
+    def __init__(self, shape, ptr, dtype="bf16"):
+        import torch
+
+        self.shape = tuple(shape)
+        self._ptr = ptr
+        self.dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def data_ptr(self):
+        return self._ptr
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+
+def test_decode_workspace_query_and_errors():
+    lib = pk.lib()
+    pool = _fake_pool(L=2, H=2, d=64, cap=100)
+    pool.n_tokens[0] = pool.n_tokens[1] = 70
+    A, lc, hq, d = 3, 2, 4, 64
+    q = _FakeT((A, lc, hq, d), 1 << 24)
+    out = _FakeT((A, lc, hq, d), 1 << 25, "f32")
+    ws = pk.agent_decode_attention([pool] * A, q, out)
+    assert ws > 0 and ws % 4 == 0
+    # suffix partials add records for every (agent, layer, q head)
+    sk = _FakeT((A, lc, 2, 16, d), 1 << 26)
+    ws2 = pk.agent_decode_attention([pool] * A, q, out, sfx_k=sk, sfx_v=sk, sfx_len=[0, 5, 16])
+    assert ws2 >= ws + A * lc * hq * (2 + d) * 4
+    with pytest.raises(pk.PolyKVError):  # sfx_len beyond capacity
+        pk.agent_decode_attention([pool] * A, q, out, sfx_k=sk, sfx_v=sk, sfx_len=[0, 5, 17])
+    with pytest.raises(pk.PolyKVError):  # heads not a multiple of kv heads
+        pk.agent_decode_attention([pool] * A, _FakeT((A, lc, 3, d), 1 << 24), _FakeT((A, lc, 3, d), 1 << 25))
+    with pytest.raises(pk.PolyKVError):  # layers beyond the pool
+        pk.agent_decode_attention([pool] * A, q, out, layer_begin=1)
+    other = _fake_pool(L=2, H=2, d=128, cap=100)
+    with pytest.raises(pk.PolyKVError):  # mixed head_dim
+        pk.agent_decode_attention([pool, pool, other], q, out)
+    pool.n_tokens[1] = 69
+    with pytest.raises(pk.PolyKVError):  # unequal token counts across the call's layers
+        pk.agent_decode_attention([pool] * A, q, out)
+    pool.n_tokens[1] = 70
+    # size is independent of pointers and grows with distinct pools
+    p2 = _fake_pool(L=2, H=2, d=64, cap=100)
+    p2.n_tokens[0] = p2.n_tokens[1] = 70
+    ws3 = pk.agent_decode_attention([pool, p2, pool], q, out)
+    assert ws3 >= ws
+    # too-small workspace is rejected before any launch
+    a, keep = pk._decode_args([pool] * A, q, out, 0)
+    size = ctypes.c_size_t(ws - 4)
+    assert lib.agent_decode_attention(ctypes.byref(a), ctypes.c_void_p(1 << 27), ctypes.byref(size), None) == -4
+    size = ctypes.c_size_t(ws)
+    assert lib.agent_decode_attention(ctypes.byref(a), ctypes.c_void_p((1 << 27) + 4), ctypes.byref(size), None) == -1
+    assert lib.agent_decode_attention(ctypes.byref(a), None, None, None) == -1
+    a.q_dtype = 9
+    assert lib.agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None) == -2
+    a.q_dtype = 1
+    a.kernel = 7
+    assert lib.agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None) == -1
+    a.kernel = 0
+    a.n_agents = 0
+    assert lib.agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None) == 0 and size.value == 0
+    del keep

@@ -1,0 +1,188 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Pool images must match the oracle bit for bit on every defined byte (K codes,
+V norms, K scales, per-head max norm, packed V code groups).  Decode outputs
+must match the fp64 oracle within 1e-3 max relative error per output vector,
+||o - o_ref||_inf / max(||o_ref||_inf, 1e-6), with fp32 accumulation on the GPU.
+Sizes span several 32-token tiles, ragged tails, mid-group appends, mixed
+bit widths, shared and distinct pools, empty and full suffixes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import attention, pool_image
+from quantized_shared_kv_amd import polykv as pk
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    pk.lib()
+    yield
+
+
+def H():
+    import gpu_helpers
+
+    return gpu_helpers
+
+
+# ---------------------------------------------------------------- quantise
+QUANT_CASES = {
+    "tiny_fp32_d64": (wl.TINY, None, None),
+    "gqa_bf16_d128_ragged": (wl.LLAMA3_8B.replace(n_layers=3, pool_tokens=300, v_bits_mode="mixed"), 3, None),
+    "mha_bf16_d64_ragged": (wl.SMOLLM2.replace(n_layers=2, n_q_heads=4, n_kv_heads=4, pool_tokens=77), 2, None),
+    "appends_mid_group": (wl.LLAMA3_8B.replace(n_layers=2, pool_tokens=157, v_bits_mode="mixed"), 2, [37, 20, 1, 99]),
+    "appends_d64_fp32": (wl.TINY.replace(n_layers=3, n_kv_heads=2, n_q_heads=2, pool_tokens=90, v_bits_mode="mixed"),
+                         3, [5, 3, 82]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(QUANT_CASES))
+def test_pool_image_bit_exact(case):
+    w, layers, chunks = QUANT_CASES[case]
+    print(f"[quant] {case}", flush=True)
+    dp, ref = H().build_pair(w, 0, layers=layers, chunks=chunks)
+    mism = H().compare_image(dp, ref)
+    assert all(v == 0 for v in mism.values()), mism
+    assert list(dp.pool.n_tokens[:ref.lay.n_layers]) == ref.n_tokens.tolist()
+
+
+def test_pool_image_zero_inputs_and_single_token():
+    h = H()
+    print("[quant] zero inputs", flush=True)
+    L, Hkv, d = 2, 2, 128
+    dp = h.DevicePool(L, Hkv, d, 64, [3, 2])
+    ref = pool_image.PoolImage(L, Hkv, d, 64, [3, 2])
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((L, Hkv, 9, d)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, 9, d)).astype(np.float32)
+    k[1] = 0.0                  # layer 1: amax = 0 -> scale 0, codes 0
+    v[0, 1, 3] = 0.0            # a zero V vector -> norm 0, codes 0
+    v[1, 0, ::2] = 0.0
+    for kk, vv in ((k[:, :, :1], v[:, :, :1]), (k[:, :, 1:], v[:, :, 1:])):  # a single-token append first
+        ref.append(0, kk, vv)
+        dp.append(0, torch.from_numpy(np.ascontiguousarray(kk)).to(h.DEV), torch.from_numpy(np.ascontiguousarray(vv)).to(h.DEV))
+    mism = h.compare_image(dp, ref)
+    assert all(x == 0 for x in mism.values()), mism
+
+
+def test_pool_bytes_do_not_depend_on_agents():
+    # the same pool bytes serve 1, 3, 10 and 15 agents: decode never writes the pool
+    h = H()
+    w = wl.LLAMA3_8B.replace(n_layers=1, pool_tokens=96, n_agents=15)
+    dp, _ = h.build_pair(w, 0)
+    before = dp.host_bytes().copy()
+    for n in (1, 3, 10, 15):
+        q, _ = h.make_queries(w, 0, range(n))
+        h.run_decode([dp.pool] * n, q)
+        assert np.array_equal(dp.host_bytes(), before)
+    assert dp.buf.numel() == pk.pool_bytes(dp.cfg)
+
+
+# ---------------------------------------------------------------- decode
+def _decode_case(w, layers, sfx_lens, kernel, splits=0, layer_begin=0, distinct=False):
+    h = H()
+    A = len(sfx_lens)
+    n_pools = A if distinct else 1
+    pairs = [h.build_pair(w, p, layers=layers) for p in range(n_pools)]
+    lc = layers - layer_begin
+    q, q32 = h.make_queries(w, 0, range(A))
+    q = q[:, layer_begin:].contiguous()
+    q32 = q32[:, layer_begin:]
+    sfx = None
+    ksf = vsf = None
+    if max(sfx_lens) > 0:
+        kd, vd, ksf0, vsf0 = h.make_suffix(w, range(A), layers)
+        sfx = (kd[:, layer_begin:].contiguous(), vd[:, layer_begin:].contiguous())
+        ksf = lambda a, l: ksf0(a, l + layer_begin)  # noqa: E731
+        vsf = lambda a, l: vsf0(a, l + layer_begin)  # noqa: E731
+    pools = [pairs[a if distinct else 0][0].pool for a in range(A)]
+    out = h.run_decode(pools, q, sfx, sfx_lens, layer_begin=layer_begin, kernel=kernel, splits=splits)
+    ref = h.oracle_decode(q32, [a if distinct else 0 for a in range(A)], [p[1] for p in pairs], ksf, vsf,
+                          sfx_lens, w.n_kv_heads, layer_begin=layer_begin)
+    assert out.shape == ref.shape and np.all(np.isfinite(out))
+    return attention.max_rel_error(out, ref), out
+
+
+KERNELS = [pk.KERNEL_VALU]
+
+DECODE_CASES = {
+    "tiny_fp32": (wl.TINY, 1, [0, 0, 0, 0], False),
+    "gqa_d128_shared_sfx": (wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=8, pool_tokens=300,
+                                                 sfx_tokens=64), 2, [0, 1, 7, 33, 64], False),
+    "mha_d64_grow": (wl.SMOLLM2.replace(n_layers=2, n_q_heads=4, n_kv_heads=4, pool_tokens=77, sfx_tokens=16), 2,
+                     [1, 9, 16], False),
+    "distinct_mixed_bits": (wl.QWEN3_32B_MIXED.replace(n_layers=3, n_q_heads=8, n_kv_heads=2, pool_tokens=100,
+                                                       sfx_tokens=16, n_agents=3, n_pools=3), 3, [16, 16, 16], True),
+    "g8_rows_over_32": (wl.QWEN3_32B_MIXED.replace(n_layers=1, n_q_heads=16, n_kv_heads=2, pool_tokens=64,
+                                                   sfx_tokens=8, n_agents=5, n_pools=1, v_bits_mode="uniform3"),
+                        1, [8, 0, 3, 8, 1], False),
+}
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", sorted(DECODE_CASES))
+def test_decode_matches_oracle(case, kernel):
+    w, layers, lens, distinct = DECODE_CASES[case]
+    print(f"[decode] {case} kernel={kernel}", flush=True)
+    err, _ = _decode_case(w, layers, lens, kernel, distinct=distinct)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("splits", [1, 3, 50])
+def test_decode_split_plans_agree(splits, kernel):
+    print(f"[decode] splits={splits} kernel={kernel}", flush=True)
+    w = wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=2, n_q_heads=8, pool_tokens=333, sfx_tokens=8)
+    err, _ = _decode_case(w, 1, [8, 2, 0], kernel, splits=splits)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_layer_subrange_and_empty_pool(kernel):
+    print(f"[decode] layer_begin / empty pool kernel={kernel}", flush=True)
+    w = wl.LLAMA3_8B.replace(n_layers=3, n_kv_heads=2, n_q_heads=4, pool_tokens=70, sfx_tokens=8)
+    err, _ = _decode_case(w, 3, [4, 8], kernel, layer_begin=1)
+    assert err <= TOL, err
+    # a pool without tokens: outputs are attention over the suffix alone
+    h = H()
+    dp = h.DevicePool(1, 2, 128, 32, [3])
+    q, q32 = h.make_queries(w.replace(n_layers=1), 0, range(2))
+    kd, vd, ksf, vsf = h.make_suffix(w.replace(n_layers=1), range(2), 1)
+    out = h.run_decode([dp.pool] * 2, q, (kd, vd), [5, 1], kernel=kernel)
+    for a, S in enumerate([5, 1]):
+        for hh in range(4):
+            ref = attention.attend(q32[a, 0, hh:hh + 1], ksf(a, 0)[hh // 2, :S], vsf(a, 0)[hh // 2, :S])
+            assert attention.max_rel_error(out[a, 0, hh:hh + 1], ref) <= TOL
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_is_deterministic_and_batch_independent(kernel):
+    print(f"[decode] determinism kernel={kernel}", flush=True)
+    h = H()
+    w = wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=8, pool_tokens=200, sfx_tokens=8)
+    dp, _ = h.build_pair(w, 0)
+    q, _ = h.make_queries(w, 0, range(4))
+    kd, vd, _, _ = h.make_suffix(w, range(4), 2)
+    a = h.run_decode([dp.pool] * 4, q, (kd, vd), [3, 8, 0, 5], kernel=kernel)
+    b = h.run_decode([dp.pool] * 4, q, (kd, vd), [3, 8, 0, 5], kernel=kernel)
+    assert np.array_equal(a, b)
+    solo = h.run_decode([dp.pool], q[1:2].contiguous(), (kd[1:2].contiguous(), vd[1:2].contiguous()), [8],
+                        kernel=kernel)
+    assert np.max(np.abs(solo[0] - a[1])) <= 1e-6 * max(1.0, np.max(np.abs(a[1])))
+
+
+def test_zero_agents_is_a_no_op():
+    h = H()
+    dp = h.DevicePool(1, 1, 64, 32, [3])
+    q = torch.zeros((0, 1, 1, 64), dtype=torch.bfloat16, device=h.DEV)
+    out = torch.zeros((0, 1, 1, 64), dtype=torch.float32, device=h.DEV)
+    assert pk.agent_decode_attention([], q, out) == 0
