@@ -88,6 +88,7 @@ def main():
     pool_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     pool = pk.pool_build(cfg, pool_buf.data_ptr(), nbytes)
     pools = [pool] * A
+    pk.pool_quantize_append(pool, 0, k_pool, v_pool)  # the workspace plan depends on the pool's token count
     ws_bytes = pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A, kernel=kernel)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()

@@ -427,7 +427,10 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             const int units = x->layer_count * hkv;
             const int tiles = std::max(1, (e.T + kTile - 1) / kTile);
             int splits = x->splits;
-            if (splits <= 0) splits = std::max(1, std::min(tiles, (2 * 256 + units - 1) / units));
+            // default split: enough workgroups to cover the 256 compute units (MFMA: one
+            // 4-wave workgroup per CU; VALU: two per CU)
+            const int target = use_mfma ? 256 : 512;
+            if (splits <= 0) splits = std::max(1, std::min(tiles, (target + units - 1) / units));
             splits = std::min(splits, tiles);
             e.chunk = (tiles + splits - 1) / splits * kTile;
             e.splits = std::max(1, (std::max(e.T, 1) + e.chunk - 1) / e.chunk);
@@ -507,14 +510,16 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         L.part = ws;
         if (L.has_sfx)
             hipLaunchKernelGGL(k_sfx_valu<D>, dim3(L.lc * L.hkv, L.n_agents), dim3(kThreads), 0, s, L);
-        if (events && i == 0) hipEventRecord(static_cast<hipEvent_t>(events[0]), s);
+        if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
             const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
             if (st != PKV_OK) return st;
         } else {
             hipLaunchKernelGGL(k_pool_valu<D>, dim3(plan.pool_wg[i]), dim3(kThreads), 0, s, L, cents);
         }
-        if (events && i + 1 == plan.launches.size()) hipEventRecord(static_cast<hipEvent_t>(events[1]), s);
+        if (events && i + 1 == plan.launches.size() &&
+            hipEventRecord(static_cast<hipEvent_t>(events[1]), s) != hipSuccess)
+            return PKV_EHIP;
         const uint64_t rows = (uint64_t)L.n_agents * L.lc * L.hq;
         hipLaunchKernelGGL(k_merge<D>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, L);
     }
@@ -534,7 +539,16 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
         if (!workspace) *workspace_bytes = 0;
         return PKV_OK;
     }
-    bool use_mfma = false;
+    // rows per pool (agents of the pool times the GQA group) decide which pool kernel can run
+    int max_rows = 0;
+    {
+        std::map<const pkv_pool*, int> cnt;
+        for (int a = 0; a < args->n_agents; ++a) max_rows = std::max(max_rows, ++cnt[args->agent_pool[a]]);
+        max_rows *= args->n_q_heads / args->agent_pool[0]->cfg.n_kv_heads;
+    }
+    const bool mfma_ok = max_rows <= 64;
+    if (args->kernel == PKV_KERNEL_MFMA && !mfma_ok) return PKV_EUNSUPPORTED;
+    const bool use_mfma = args->kernel == PKV_KERNEL_MFMA || (args->kernel == PKV_KERNEL_DEFAULT && mfma_ok);
     Plan plan;
     make_plan(args, use_mfma, &plan);
     const size_t need = plan.ws_floats * sizeof(float);

@@ -112,7 +112,7 @@ def _decode_case(w, layers, sfx_lens, kernel, splits=0, layer_begin=0, distinct=
     return attention.max_rel_error(out, ref), out
 
 
-KERNELS = [pk.KERNEL_VALU]
+KERNELS = [pk.KERNEL_VALU, pk.KERNEL_MFMA]
 
 DECODE_CASES = {
     "tiny_fp32": (wl.TINY, 1, [0, 0, 0, 0], False),
