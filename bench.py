@@ -37,7 +37,60 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                             "pool_decode_traffic.json"))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the traffic summary")
     return ap.parse_args()
+
+
+def _counter_per_dispatch(path, name_part, counter):
+    import csv
+
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(paths, out_path, kernel_variant, workload):
+    """HBM bytes per pool-kernel launch from FETCH_SIZE and WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by what it reads for a plain copy of known size
+    (256 MiB read and 256 MiB written per launch).
+    """
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = paths
+    f_pool, nf = _counter_per_dispatch(fetch_csv, "k_pool_mfma", "FETCH_SIZE")
+    w_pool, nw = _counter_per_dispatch(write_csv, "k_pool_mfma", "WRITE_SIZE")
+    f_copy, _ = _counter_per_dispatch(cfetch_csv, "opy", "FETCH_SIZE")
+    w_copy, _ = _counter_per_dispatch(cwrite_csv, "opy", "WRITE_SIZE")
+    n = 256 << 20
+    f_scale = n / (f_copy * 1024.0)
+    w_scale = n / (w_copy * 1024.0)
+    res = {"workload": workload, "kernel_variant": kernel_variant,
+           "fetch_kib_per_dispatch": f_pool, "write_kib_per_dispatch": w_pool, "dispatches": [nf, nw],
+           "copy_fetch_kib": f_copy, "copy_write_kib": w_copy, "fetch_scale": f_scale, "write_scale": w_scale,
+           "bytes_per_launch": f_pool * 1024.0 * f_scale + w_pool * 1024.0 * w_scale}
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 256 MiB read + 256 MiB written per launch."""
+    import torch
+
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
 def log(msg):
@@ -46,6 +99,14 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.pmc_summary:
+        import workloads as wl
+
+        pmc_summary(args.pmc_summary, args.traffic_json, args.kernel, wl.LLAMA3_8B.name)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
               file=sys.stderr)

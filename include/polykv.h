@@ -148,9 +148,9 @@ typedef struct {
     const int32_t* sfx_len;           /* host [n_agents]: native tokens agent a attends to; may be NULL (all 0) */
     float* out;                       /* device fp32 [n_agents][layer_count][n_q_heads][head_dim] */
     int32_t kernel;                   /* pool kernel: PKV_KERNEL_DEFAULT (MFMA when every pool has
-                                         at most 64 rows = agents * q heads per kv head, else VALU),
-                                         PKV_KERNEL_VALU, or PKV_KERNEL_MFMA (PKV_EUNSUPPORTED if a
-                                         pool has more than 64 rows) */
+                                         at most 64 rows = agents * q heads per kv head, 48 with fp32
+                                         queries, else VALU), PKV_KERNEL_VALU, or PKV_KERNEL_MFMA
+                                         (PKV_EUNSUPPORTED above those row counts) */
     int32_t splits;                   /* token splits per (pool, layer, kv head); 0 = automatic */
     void* const* pool_events;         /* optional instrumentation: NULL, or two hipEvent_t recorded on
                                          the stream right before the first and right after the last

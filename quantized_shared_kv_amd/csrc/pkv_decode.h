@@ -45,6 +45,7 @@ struct DecodeLaunch {
     int32_t l0, lc;         // first pool layer of the call, layers in the call
     int32_t sfx_cap;
     int32_t has_sfx;
+    int32_t fused;          // the pool kernel finishes the outputs itself (one split everywhere)
     float sm_log2;          // softmax scale * log2(e)
 };
 

@@ -36,6 +36,8 @@ struct Centroids {
     float c[3][16];
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float ld_elem(const void* p, int dtype, uint64_t i) {
     if (dtype == PKV_BF16) {
         const uint16_t b = static_cast<const uint16_t*>(p)[i];
@@ -286,6 +288,156 @@ __global__ void __launch_bounds__(kThreads) k_sfx_valu(DecodeLaunch a) {
     }
 }
 
+// Native suffix attention, one wavefront per (launch agent, layer, kv head):
+// lanes own tokens for the scores (bf16 K rows times bf16 queries with
+// v_dot2c_f32_bf16, exact products, fp32 accumulation; any fp32 operand takes a
+// plain fp32 FMA path), the softmax state is kept per row across the wave, and for the value
+// sum each lane owns D/64 dimensions while the probabilities of a 64-token
+// chunk are broadcast from LDS.  Rows are the kv head's q heads (G <= 8 per
+// pass; larger groups take several passes).
+constexpr int kSfxRows = 8;
+
+template <int D, bool BF16>  // BF16: bf16 queries and bf16 suffix (dot2 path)
+__device__ void sfx_wave(const DecodeLaunch& a, int unit, float* pbuf, uint32_t* qbuf) {
+    constexpr int EPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int g = unit % a.hkv;
+    const int lj = (unit / a.hkv) % a.lc;
+    const int k = unit / (a.hkv * a.lc);
+    const int agent = a.agent_id[k];
+    const int S = a.sfx_len[k];
+    const uint64_t tok0 = (((uint64_t)agent * a.lc + lj) * a.hkv + g) * (uint64_t)a.sfx_cap;
+    for (int r0 = 0; r0 < a.G; r0 += kSfxRows) {
+        const int nr = min(kSfxRows, a.G - r0);
+        // queries of this pass: bf16 pairs (BF16) or fp32 values, in LDS
+        for (int idx = lane; idx < kSfxRows * D; idx += 64) {
+            const int r = idx / D, i = idx % D;
+            float x = 0.0f;
+            if (r < nr) x = ld_elem(a.q, a.q_dtype, (((uint64_t)agent * a.lc + lj) * a.hq + g * a.G + r0 + r) * D + i);
+            if (BF16) {
+                // the bf16 query's bits (x is its exact fp32 widening)
+                reinterpret_cast<uint16_t*>(qbuf)[r * D + i] = static_cast<uint16_t>(__float_as_uint(x) >> 16);
+            } else {
+                reinterpret_cast<float*>(qbuf)[r * D + i] = x;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        float m[kSfxRows], l[kSfxRows], acc[kSfxRows][EPL];
+#pragma unroll
+        for (int r = 0; r < kSfxRows; ++r) {
+            m[r] = -INFINITY;
+            l[r] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[r][e] = 0.0f;
+        }
+        for (int c0 = 0; c0 < S; c0 += 64) {
+            const int t = c0 + lane;
+            const bool ok = t < S;
+            float sc[kSfxRows];
+#pragma unroll
+            for (int r = 0; r < kSfxRows; ++r) sc[r] = 0.0f;
+            if (ok) {
+                if (BF16) {
+                    const uint4* krow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.sfx_k) + (tok0 + t) * D);
+#pragma unroll 4
+                    for (int c = 0; c < D / 8; ++c) {
+                        const uint4 kv = krow[c];
+#pragma unroll
+                        for (int r = 0; r < kSfxRows; ++r) {
+                            if (r < nr) {
+                                const uint4 qv = reinterpret_cast<const uint4*>(qbuf)[(r * D) / 8 + c];
+                                float s2 = sc[r];
+                                s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv.x), __builtin_bit_cast(bf16x2_t, qv.x), s2, false);
+                                s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv.y), __builtin_bit_cast(bf16x2_t, qv.y), s2, false);
+                                s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv.z), __builtin_bit_cast(bf16x2_t, qv.z), s2, false);
+                                s2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kv.w), __builtin_bit_cast(bf16x2_t, qv.w), s2, false);
+                                sc[r] = s2;
+                            }
+                        }
+                    }
+                } else {
+                    for (int c = 0; c < D; ++c) {
+                        const float kv = ld_elem(a.sfx_k, a.sfx_dtype, (tok0 + t) * D + c);
+#pragma unroll
+                        for (int r = 0; r < kSfxRows; ++r)
+                            if (r < nr) sc[r] += kv * reinterpret_cast<const float*>(qbuf)[r * D + c];
+                    }
+                }
+            }
+            // online softmax per row over this chunk (log2 units)
+#pragma unroll
+            for (int r = 0; r < kSfxRows; ++r) {
+                if (r >= nr) break;
+                const float x = ok ? sc[r] * a.sm_log2 : -INFINITY;
+                float mx = x;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                const float mnew = fmaxf(m[r], mx);
+                const float alpha = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mnew);
+                const float p = ok ? exp2f(x - mnew) : 0.0f;
+                float ps = p;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
+                l[r] = l[r] * alpha + ps;
+                m[r] = mnew;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[r][e] *= alpha;
+                pbuf[lane * kSfxRows + r] = p;
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int nt = min(64, S - c0);
+            for (int tt = 0; tt < nt; ++tt) {
+                float v[EPL];
+                const uint64_t vo = (tok0 + c0 + tt) * D + EPL * lane;
+                if (BF16) {
+                    if (EPL == 2) {
+                        const uint32_t two = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.sfx_v) + vo)[0];
+                        v[0] = __uint_as_float(two << 16);
+                        v[EPL - 1] = __uint_as_float(two & 0xffff0000u);
+                    } else {
+                        v[0] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.sfx_v)[vo]) << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) v[e] = ld_elem(a.sfx_v, a.sfx_dtype, vo + e);
+                }
+                const float4 p03 = reinterpret_cast<const float4*>(pbuf)[tt * 2];
+                const float4 p47 = reinterpret_cast<const float4*>(pbuf)[tt * 2 + 1];
+                const float pr[kSfxRows] = {p03.x, p03.y, p03.z, p03.w, p47.x, p47.y, p47.z, p47.w};
+#pragma unroll
+                for (int r = 0; r < kSfxRows; ++r)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[r][e] += pr[r] * v[e];
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        for (int r = 0; r < nr; ++r) {
+            float* rec = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + g * a.G + r0 + r) * (2 + D);
+            if (lane == 0) {
+                rec[0] = m[r];
+                rec[1] = l[r];
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) rec[2 + EPL * lane + e] = acc[r][e];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// grid ceil(n_agents * lc * hkv / 4), 256 threads = 4 wavefronts, one unit each
+template <int D>
+__global__ void __launch_bounds__(256) k_sfx(DecodeLaunch a) {
+    __shared__ __align__(16) float pbuf[4][64 * kSfxRows];
+    __shared__ __align__(16) uint32_t qbuf[4][kSfxRows * D];
+    const int wave = threadIdx.x >> 6;
+    const int unit = blockIdx.x * 4 + wave;
+    if (unit >= a.n_agents * a.lc * a.hkv) return;
+    if (a.sfx_dtype == PKV_BF16 && a.q_dtype == PKV_BF16)
+        sfx_wave<D, true>(a, unit, pbuf[wave], qbuf[wave]);
+    else
+        sfx_wave<D, false>(a, unit, pbuf[wave], qbuf[wave]);
+}
+
 // One wavefront per output row (launch agent, layer, q head): combine the
 // pool's split records, apply the inverse FWHT (H / d) to the rotated-domain
 // accumulator, fold in the suffix record and normalise.
@@ -508,10 +660,15 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
     for (size_t i = 0; i < plan.launches.size(); ++i) {
         DecodeLaunch L = plan.launches[i];
         L.part = ws;
-        if (L.has_sfx)
-            hipLaunchKernelGGL(k_sfx_valu<D>, dim3(L.lc * L.hkv, L.n_agents), dim3(kThreads), 0, s, L);
+        if (L.has_sfx) {
+            const int units = L.n_agents * L.lc * L.hkv;
+            hipLaunchKernelGGL(k_sfx<D>, dim3((units + 3) / 4), dim3(kThreads), 0, s, L);
+        }
         if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
+            // one split per (pool, layer, kv head): the MFMA kernel finishes the rows itself
+            L.fused = 1;
+            for (int p = 0; p < L.n_pools; ++p) L.fused &= L.pools[p].splits == 1;
             const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
             if (st != PKV_OK) return st;
         } else {
@@ -520,8 +677,10 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         if (events && i + 1 == plan.launches.size() &&
             hipEventRecord(static_cast<hipEvent_t>(events[1]), s) != hipSuccess)
             return PKV_EHIP;
-        const uint64_t rows = (uint64_t)L.n_agents * L.lc * L.hq;
-        hipLaunchKernelGGL(k_merge<D>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, L);
+        if (!L.fused) {
+            const uint64_t rows = (uint64_t)L.n_agents * L.lc * L.hq;
+            hipLaunchKernelGGL(k_merge<D>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, L);
+        }
     }
     return launch_status();
 }
@@ -546,7 +705,8 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
         for (int a = 0; a < args->n_agents; ++a) max_rows = std::max(max_rows, ++cnt[args->agent_pool[a]]);
         max_rows *= args->n_q_heads / args->agent_pool[0]->cfg.n_kv_heads;
     }
-    const bool mfma_ok = max_rows <= 64;
+    // fp32 queries need hi + lo query operands; above 48 rows they do not fit the registers
+    const bool mfma_ok = max_rows <= (args->q_dtype == PKV_F32 ? 48 : 64);
     if (args->kernel == PKV_KERNEL_MFMA && !mfma_ok) return PKV_EUNSUPPORTED;
     const bool use_mfma = args->kernel == PKV_KERNEL_MFMA || (args->kernel == PKV_KERNEL_DEFAULT && mfma_ok);
     Plan plan;

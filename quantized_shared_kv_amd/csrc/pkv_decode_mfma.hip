@@ -10,13 +10,23 @@
 //
 // One workgroup of 4 wavefronts handles one (pool, layer, kv head, token
 // split); each wavefront streams every 4th 32-token step of the split and
-// keeps all rows (up to 64, in RT tiles of 16) in registers:
+// keeps all rows (up to 64, in RT tiles of 16) in its accumulators:
 //
-//   S^T[32 tok][16 rows] = Kq (int8 -> exact fp16) x Q^T (fp16)   2*RT*(d/32) MFMAs
-//   x = S * (Ks[t] * sigma * log2 e); lazy online softmax (rescale only when a
-//   row max grows by more than 2^8); w = p * Vn[t] * 2^(7-e) with e from the
-//   per-head max norm, so w < 2^15, split into fp16 hi + lo parts
+//   S^T[32 tok][16 rows] = (1152 + Kq as exact fp16) x Q^T (fp16), accumulator
+//   started at -1152 * sum(q)                                      2*RT*(d/32) MFMAs
+//   x = S * (Ks[t] * sigma * log2 e) - mref with a fixed per-row reference (see
+//   below); w = p * Vn[t] * 2^(7-e) with e from the per-head max norm, so
+//   w < 2^15, split into fp16 hi + lo parts
 //   acc[16 rows][16 dims] += (Wh + Wl)[16][32 tok] x C[32 tok][16 dims]   2*RT*(d/16) MFMAs
+//
+// Memory: every wavefront owns a 4-stage ring in LDS filled by gfx950
+// direct-to-LDS loads (global_load_lds, 16/12/4 bytes per lane; 12- and 16-byte
+// loads place lane l's bytes at lane * 16), three steps ahead of use, so ~70 KB
+// per CU are in flight without holding registers.
+// The waits are explicit vmcnt counts and the ring is read by inline-asm
+// ds_reads (the compiler would otherwise wait for every load before each
+// LDS read).  K is fetched lane-owned (each lane's 16-byte pieces are exactly
+// what it later reads), so those LDS reads are contiguous across the wave.
 //
 // Lane layout (16x16x32: A row / B column = lane & 15, k-group = lane >> 4,
 // D rows 4*(lane>>4) + j): the S^T accumulator of lane (g, r) holds tokens
@@ -31,11 +41,15 @@
 // the same bank; each LUT read is one B-operand register.
 //
 // The rotated-domain accumulator and (m, l) of every row are merged across the
-// 4 wavefronts in LDS (in a fixed order, so results are deterministic) and
-// written as partial records; k_merge applies the one inverse FWHT per row.
+// 4 wavefronts in LDS in a fixed order (deterministic).  With one split per
+// (layer, kv head) the workgroup then finishes the rows itself: one inverse
+// FWHT per row, the agent's suffix record folded in, the output written.
+// Otherwise it writes partial records for k_merge.
 #include <cstring>
+#include <type_traits>
 
 #include "pkv_decode.h"
+#include "pkv_lanes.h"
 
 namespace pkv {
 namespace {
@@ -46,9 +60,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kStep = 32;         // tokens per wavefront step
-constexpr float kLazy = 8.0f;     // log2 growth of a row max tolerated before rescaling
+constexpr int kStages = 4;        // LDS ring depth per wavefront (kStages - 1 steps in flight)
+constexpr float kLazy = 8.0f;     // scores may exceed the reference by up to 2^8 (fp16 weights)
+constexpr float kMargin = 8.0f;   // reference = first step's row max + this (log2 units)
 constexpr int kLutCopies = 32;
 constexpr int kWeightExp = 7;     // weights are scaled into [0, 2^15)
+constexpr int kStageBytes = 32 * 128 + 64 * 32 + 256;  // K + V codes + norms/scales, largest case
 
 struct CentArg {
     float c[3][16];
@@ -57,7 +74,28 @@ struct CentArg {
 union H8 {
     half8 h;
     uint32_t u[4];
+    uint4 v;
 };
+
+// Per-wavefront ring of the upcoming steps, filled by direct-to-LDS loads.
+// During the token loop: the per-wavefront rings filled by direct-to-LDS loads and
+// the LUT of centroid pairs.  After it: every wavefront's rotated-domain
+// accumulator tile [64 rows][D], combined in a fixed order.
+constexpr int kMaxRows = 64;
+struct LoopLds {
+    uint8_t ring[kWaves][kStages][kStageBytes];
+    uint32_t lut[256 * kLutCopies];
+};
+union BigLds {
+    LoopLds loop;
+    float accs[kWaves * kMaxRows * 128];
+};
+__shared__ __align__(16) BigLds g_big;
+// fp16 query B operands of every lane: [RT][KS][64 lanes] x 16 bytes.
+__shared__ __align__(16) uint4 g_qop[4 * 4 * 64];
+__shared__ float g_m[kWaves][64];
+__shared__ float g_l[kWaves][64];
+__shared__ int g_flag;
 
 __device__ __forceinline__ int find_pool_m(const DecodeLaunch& a, int wg) {
     int p = 0;
@@ -70,15 +108,32 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 4 int8 (two's complement) -> 4 exact fp16: bytes u = x + 128 are placed in the
-// mantissa of 1024 (fp16 0x6400), giving 1024 + u, then 1152 is subtracted.
-__device__ __forceinline__ void i8x4_to_h4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 4 int8 (two's complement) -> 4 fp16 holding 1152 + k exactly: the bytes u = k + 128
+// are placed in the mantissa of 1024 (fp16 0x6400), giving 1024 + u.  The constant
+// 1152 * sum(q) this adds to every score is subtracted by starting the MFMA
+// accumulator at -1152 * sum(q).
+__device__ __forceinline__ void i8x4_to_h4_offset(uint32_t w, uint32_t& lo, uint32_t& hi) {
     const uint32_t u = w ^ 0x80808080u;
-    const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-    const half2v off = {(_Float16)(-1152.0f), (_Float16)(-1152.0f)};
-    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) + off);
-    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, b) + off);
+    lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+}
+
+// v_max3_f32 without the NaN-quieting the compiler adds around fmaxf of loaded or
+// MFMA-produced values (the operands here are finite or -inf)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 template <int NBYTES>
@@ -86,32 +141,13 @@ struct Chunk {
     uint32_t w[NBYTES / 4];
 };
 
-// Load NBYTES (8, 12, 16, 24 or 32) of V codes; the address is NBYTES-multiple aligned
-// within a 256-byte aligned region, so 8-byte pieces are 8-aligned when NBYTES % 8 == 0.
-template <int NBYTES>
-__device__ __forceinline__ Chunk<NBYTES> load_chunk(const uint8_t* p) {
-    Chunk<NBYTES> c;
-    if constexpr (NBYTES % 16 == 0) {
-#pragma unroll
-        for (int i = 0; i < NBYTES / 16; ++i) {
-            const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-            c.w[4 * i] = v.x;
-            c.w[4 * i + 1] = v.y;
-            c.w[4 * i + 2] = v.z;
-            c.w[4 * i + 3] = v.w;
-        }
-    } else if constexpr (NBYTES % 8 == 0) {
-#pragma unroll
-        for (int i = 0; i < NBYTES / 8; ++i) {
-            const uint2 v = reinterpret_cast<const uint2*>(p)[i];
-            c.w[2 * i] = v.x;
-            c.w[2 * i + 1] = v.y;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NBYTES / 4; ++i) c.w[i] = reinterpret_cast<const uint32_t*>(p)[i];
-    }
-    return c;
+// v_bfe_u32 kept opaque: the compiler would otherwise fold the later scaling of the
+// field into its shift and need a separate mask
+template <int OFF, int W>
+__device__ __forceinline__ uint32_t bfe(uint32_t w) {
+    uint32_t r;
+    asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "i"(OFF), "i"(W));
+    return r;
 }
 
 // 2b-bit field at bit position P of the chunk (P, b compile-time).
@@ -119,59 +155,133 @@ template <int NBYTES, int P, int W>
 __device__ __forceinline__ uint32_t field(const Chunk<NBYTES>& c) {
     constexpr int wi = P >> 5, sh = P & 31;
     if constexpr (sh + W <= 32) {
-        return (c.w[wi] >> sh) & ((1u << W) - 1u);
+        return bfe<sh, W>(c.w[wi]);
     } else {
-        return __builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh) & ((1u << W) - 1u);
+        return bfe<0, W>(__builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh));
     }
 }
 
+// lutl = this lane's copy of the LUT (lut + lane % kLutCopies): entry e at lutl[e * kLutCopies]
 template <int NBYTES, int BITS, int NBI, int PI>
-__device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, const uint32_t* lut, uint32_t lane_off) {
+__device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, const uint32_t* lutl) {
     const uint32_t idx = field<NBYTES, 8 * BITS * NBI + 2 * BITS * PI, 2 * BITS>(c);
-    return lut[idx * kLutCopies + lane_off];
+    return lutl[idx * kLutCopies];
 }
 
 template <int NBYTES, int BITS, int NBI>
-__device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, const uint32_t* lut, uint32_t lane_off) {
+__device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, const uint32_t* lutl) {
     H8 r;
-    r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lut, lane_off);
-    r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lut, lane_off);
-    r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lut, lane_off);
-    r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lut, lane_off);
+    r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lutl);
+    r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lutl);
+    r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lutl);
+    r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lutl);
     return r.h;
 }
 
-template <int D, int RT, int BITS, int NBI = 0>
-__device__ __forceinline__ void pv_all(f32x4 (&acc)[RT][D / 16], const half8 (&Wh)[RT], const half8 (&Wl)[RT],
-                                       const Chunk<D / 16 * BITS>& c, const uint32_t* lut, uint32_t lane_off) {
-    if constexpr (NBI < D / 16) {
-        const half8 vb = decode_b<D / 16 * BITS, BITS, NBI>(c, lut, lane_off);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            acc[rt][NBI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wh[rt], vb, acc[rt][NBI], 0, 0, 0);
-            acc[rt][NBI] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Wl[rt], vb, acc[rt][NBI], 0, 0, 0);
-        }
-        pv_all<D, RT, BITS, NBI + 1>(acc, Wh, Wl, c, lut, lane_off);
+template <int CB, int BITS, int NBI = 0>
+__device__ __forceinline__ void decode_all(half8 (&vb)[CB / BITS], const Chunk<CB>& c, const uint32_t* lutl) {
+    if constexpr (NBI < CB / BITS) {
+        vb[NBI] = decode_b<CB, BITS, NBI>(c, lutl);
+        decode_all<CB, BITS, NBI + 1>(vb, c, lutl);
     }
 }
 
-struct Smem {
-    union {
-        uint32_t lut[256 * kLutCopies];  // fp16 centroid pairs, replicated
-        float accbuf[64 * 128];          // cross-wave merge of the accumulators
-    };
-    float m[kWaves][64];
-    float l[kWaves][64];
+// Direct-to-LDS load: every lane's `SIZE` bytes at gsrc land at ldst + lane * SIZE.
+template <int SIZE>
+__device__ __forceinline__ void dma(const void* gsrc, void* ldst) {
+    auto* l = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(ldst));
+    if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(gsrc, l, 16, 0, 0);
+    else if constexpr (SIZE == 12) __builtin_amdgcn_global_load_lds(gsrc, l, 12, 0, 0);
+    else __builtin_amdgcn_global_load_lds(gsrc, l, 4, 0, 0);
+}
+
+// All ring reads of one step in a single asm statement that ends with
+// s_waitcnt lgkmcnt(0), so no value can be used before it has arrived.
+// ka: this lane's K pieces (kr[i] at ka + i * 1024); va: its V code pieces (at
+// va + i * VSTRIDE); na: the norms of its 8 tokens (ns[0..1]) and their scales
+// (ns[2..3], 128 bytes on).
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+template <int NK, int CB>
+__device__ __forceinline__ void read_step(uint32_t ka, uint32_t va, uint32_t na, uint4 (&kr)[NK],
+                                          uint32_t (&cw)[CB / 4], uint4 (&ns)[4]) {
+    if constexpr (NK == 2 && CB == 8) {
+        
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b32 %2, %[va] offset:0\n\tds_read_b32 %3, %[va] offset:256\n\tds_read_b128 %4, %[na] offset:0\n\tds_read_b128 %5, %[na] offset:16\n\tds_read_b128 %6, %[na] offset:128\n\tds_read_b128 %7, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        
+    }
+    if constexpr (NK == 2 && CB == 12) {
+        u32x3 v0;
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b96 %2, %[va]\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        cw[0] = v0[0]; cw[1] = v0[1]; cw[2] = v0[2];
+    }
+    if constexpr (NK == 2 && CB == 16) {
+        uint4 v0;
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[va]\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w;
+    }
+    if constexpr (NK == 4 && CB == 16) {
+        uint4 v0;
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va]\n\tds_read_b128 %5, %[na] offset:0\n\tds_read_b128 %6, %[na] offset:16\n\tds_read_b128 %7, %[na] offset:128\n\tds_read_b128 %8, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w;
+    }
+    if constexpr (NK == 4 && CB == 24) {
+        u32x3 v0, v1;
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b96 %4, %[va] offset:0\n\tds_read_b96 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(v1), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        cw[0] = v0[0]; cw[1] = v0[1]; cw[2] = v0[2]; cw[3] = v1[0]; cw[4] = v1[1]; cw[5] = v1[2];
+    }
+    if constexpr (NK == 4 && CB == 32) {
+        uint4 v0, v1;
+        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va] offset:0\n\tds_read_b128 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(v1), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
+                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                     : "memory");
+        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w; cw[4] = v1.x; cw[5] = v1.y; cw[6] = v1.z; cw[7] = v1.w;
+    }
+}
+
+template <int D, int BITS>
+struct StageLayout {
+    static constexpr int NK = D / 32;            // 16-byte K pieces per lane (2 tiles x D/64)
+    static constexpr int CB = D / 16 * BITS;     // V code bytes per lane
+    // V pieces per lane: 4-byte loads land lane-contiguous; 12- and 16-byte loads
+    // land at lane * 16, so every piece of lane l sits at VOFF + i * VSTRIDE + l * VLANE
+    static constexpr int NV = (CB == 12 || CB == 16) ? 1 : 2;
+    static constexpr int VLANE = (CB == 8) ? 4 : 16;
+    static constexpr int VSTRIDE = 64 * VLANE;
+    static constexpr int KOFF = 0;
+    static constexpr int VOFF = NK * 1024;
+    static constexpr int NOFF = VOFF + NV * VSTRIDE;  // norms [32] then scales [32]
+    static constexpr int NDMA = NK + NV + 1;          // direct-to-LDS instructions per stage
+    static_assert(NOFF + 256 <= kStageBytes, "stage overflow");
 };
 
+// Always inlined: an out-of-line body would receive the launch struct by reference,
+// which makes every lane copy it to scratch.
 template <int D, int RT, int BITS, bool QSPLIT>
-__device__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents, Smem& sm) {
+__device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents) {
+    using SL = StageLayout<D, BITS>;
     constexpr int NB = D / 16;   // PV column tiles
     constexpr int KS = D / 32;   // QK k-steps
     constexpr int DL = D / 4;    // K bytes per lane per token
-    constexpr int CB = NB * BITS;  // V code bytes per lane per step
+    constexpr int CB = SL::CB;   // V code bytes per lane per step
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int rl = lane & 15, lg = lane >> 4;
 
     const int p = find_pool_m(a, blockIdx.x);
@@ -194,21 +304,56 @@ __device__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents, Smem
     frexpf(vmax, &ex);
     // vn * nu < 2^7, so w = p * vn * nu < 2^15 fits fp16 while keeping the lo part of
     // small weights out of the fp16 subnormal range
-    const float nu = ldexpf(1.0f, (vmax > 0.0f ? -ex : 0) + kWeightExp);
+    const int lnu = (vmax > 0.0f ? -ex : 0) + kWeightExp;
+    const float nu = ldexpf(1.0f, lnu);
 
-    // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
-    {
-        const float* c = cents.c[BITS - 2];
-        constexpr int NE = 1 << (2 * BITS);
-        for (int i = tid; i < NE * kLutCopies; i += 256) {
-            const int e = i / kLutCopies;
-            sm.lut[i] = pack_h2(c[e & ((1 << BITS) - 1)], c[e >> BITS]);
+    const int tb = sp * P.chunk;
+    const int te = min(P.T, tb + P.chunk);
+    const int nsteps = te > tb ? (te - tb + kStep - 1) / kStep : 0;
+    const int my_steps = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+    // K row of this lane in tile u: token 8*(rl>>2) + 4u + (rl&3), bytes lg*DL .. lg*DL + DL
+    const int ktok0 = 8 * (rl >> 2) + (rl & 3);
+    uint8_t* ring = &g_big.loop.ring[wave][0][0];
+
+    auto issue = [&](int it) {  // DMA of this wavefront's it-th step into ring slot it % kStages
+        const int t0 = tb + (wave + it * kWaves) * kStep;
+        uint8_t* st = ring + (it % kStages) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < SL::NK; ++i) {
+            const int u = i / (DL / 16), h = i % (DL / 16);
+            dma<16>(kq + (uint64_t)(t0 + ktok0 + 4 * u) * D + lg * DL + 16 * h, st + SL::KOFF + i * 1024);
         }
-    }
+        // this lane's code chunk: bytes [CB * lane, CB * lane + CB) of the step's 4 groups
+        const uint8_t* vsrc = vc + (uint64_t)(t0 / kGroupTokens) * (D * BITS) + CB * lane;
+        if constexpr (CB == 8) {
+            dma<4>(vsrc, st + SL::VOFF);
+            dma<4>(vsrc + 4, st + SL::VOFF + SL::VSTRIDE);
+        } else if constexpr (CB == 12) {
+            dma<12>(vsrc, st + SL::VOFF);
+        } else if constexpr (CB == 16) {
+            dma<16>(vsrc, st + SL::VOFF);
+        } else if constexpr (CB == 24) {
+            dma<12>(vsrc, st + SL::VOFF);
+            dma<12>(vsrc + 12, st + SL::VOFF + SL::VSTRIDE);
+        } else {
+            dma<16>(vsrc, st + SL::VOFF);
+            dma<16>(vsrc + 16, st + SL::VOFF + SL::VSTRIDE);
+        }
+        const float* nsrc = lane < 32 ? vn + t0 + lane : ks + t0 + (lane - 32);
+        dma<4>(nsrc, st + SL::NOFF);
+    };
 
-    // queries as B operands: lane (lg, rl) holds row 16 rt + rl, dims lg*DL + 8 ks + i
-    half8 qb[RT][KS];
+    // start the ring (kStages - 1 steps ahead) first, so the loads overlap the set-up
+#pragma unroll
+    for (int it = 0; it < kStages - 1; ++it)
+        if (it < my_steps) issue(it);
+
+    // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i);
+    // bf16 values convert exactly (8 significant bits) within fp16's range, fp32
+    // values are split into fp16 hi + lo operands
+    half8 qreg[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
     half8 qlo[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
+    float qoff[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = 16 * rt + rl;
@@ -216,7 +361,8 @@ __device__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents, Smem
         const int rr = ok ? rho : 0;
         const int agent = a.agent_id[P.agent0 + rr / a.G];
         const int head = g * a.G + rr % a.G;
-        const uint64_t qoff = (((uint64_t)agent * a.lc + lj) * a.hq + head) * D + lg * DL;
+        const uint64_t qo = (((uint64_t)agent * a.lc + lj) * a.hq + head) * D + lg * DL;
+        float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             H8 hv, lv;
@@ -226,226 +372,405 @@ __device__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents, Smem
                 if (ok) {
                     if (a.q_dtype == PKV_BF16) {
                         const uint32_t two = reinterpret_cast<const uint32_t*>(
-                            static_cast<const uint16_t*>(a.q) + qoff + 8 * k)[i];
+                            static_cast<const uint16_t*>(a.q) + qo + 8 * k)[i];
                         x0 = __uint_as_float(two << 16);
                         x1 = __uint_as_float(two & 0xffff0000u);
                     } else {
-                        const float2 two = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qoff + 8 * k)[i];
+                        const float2 two = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qo + 8 * k)[i];
                         x0 = two.x;
                         x1 = two.y;
                     }
                 }
                 hv.u[i] = pack_h2(x0, x1);
+                const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
+                sum += (float)hh[0] + (float)hh[1];
                 if constexpr (QSPLIT) {
-                    const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
                     lv.u[i] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                    const half2v ll = __builtin_bit_cast(half2v, lv.u[i]);
+                    sum += (float)ll[0] + (float)ll[1];
                 }
             }
-            qb[rt][k] = hv.h;
-            if constexpr (QSPLIT) qlo[rt][k] = lv.h;
+            if constexpr (QSPLIT) {
+                qreg[rt][k] = hv.h;
+                qlo[rt][k] = lv.h;
+            } else if (wave == 0) {
+                g_qop[(rt * KS + k) * 64 + lane] = hv.v;
+            }
+        }
+        // -1152 * sum of the row's fp16 query values: cancels the offset carried by K
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        qoff[rt] = -1152.0f * sum;
+    }
+    // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
+    {
+        const float* c = cents.c[BITS - 2];
+        constexpr int NE = 1 << (2 * BITS);
+        for (int i = tid; i < NE * kLutCopies; i += 256) {
+            const int e = i / kLutCopies;
+            g_big.loop.lut[i] = pack_h2(c[e & ((1 << BITS) - 1)], c[e >> BITS]);
         }
     }
-    __syncthreads();  // LUT ready
+    __syncthreads();  // LUT and query operands ready
 
-    float m[RT], lsum[RT];
-    f32x4 acc[RT][NB];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        m[rt] = -INFINITY;
-        lsum[rt] = 0.0f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
-    const int tb = sp * P.chunk;
-    const int te = min(P.T, tb + P.chunk);
-    const int nsteps = te > tb ? (te - tb + kStep - 1) / kStep : 0;
+    const uint32_t* lutl = g_big.loop.lut + (lane & (kLutCopies - 1));
+    const uint32_t ring_a = lds_addr(ring);
     const float fs = a.sm_log2;
-    const uint32_t lane_off = lane & (kLutCopies - 1);
-    const uint32_t* lut = sm.lut;
-    // K row of this lane in tile u: token 8*(rl>>2) + 4u + (rl&3), bytes lg*DL .. lg*DL + DL
-    const int ktok0 = 8 * (rl >> 2) + (rl & 3);
 
-    for (int st = wave; st < nsteps; st += kWaves) {
-        const int t0 = tb + st * kStep;
-        // ---- loads
-        uint4 kr[2][DL / 16];
+    // wait until the loads of this wavefront's step `it` have landed (steps are
+    // issued in order, kStages - 1 ahead of use)
+    auto wait_step = [&](int it) {
+        const int ahead = min(my_steps - 1 - it, kStages - 2);  // steps issued after it
+        if (ahead >= 2) wait_vmcnt<2 * SL::NDMA>();
+        else if (ahead == 1) wait_vmcnt<SL::NDMA>();
+        else wait_vmcnt<0>();
+    };
+    // the ring slot of step `it`: K as fp16 operands (1152 + k, exact; the offset is
+    // removed by the accumulator init), V code chunk, norms and scales
+    auto read_slot = [&](int it, half8 (&ka)[2][KS], Chunk<CB>& ch, uint4 (&ns)[4]) {
+        const uint32_t sa = ring_a + (it % kStages) * kStageBytes;
+        uint4 kr[SL::NK];
+        read_step<SL::NK, CB>(sa + SL::KOFF + lane * 16, sa + SL::VOFF + lane * SL::VLANE, sa + SL::NOFF + 32 * lg,
+                              kr, ch.w, ns);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint4* src = reinterpret_cast<const uint4*>(kq + (uint64_t)(t0 + ktok0 + 4 * u) * D + lg * DL);
-#pragma unroll
-            for (int i = 0; i < DL / 16; ++i) kr[u][i] = src[i];
-        }
-        const Chunk<CB> ch = load_chunk<CB>(vc + ((uint64_t)(t0 / kGroupTokens + lg) * 16 + rl) * CB);
-        const float4 n0 = reinterpret_cast<const float4*>(vn + t0 + 8 * lg)[0];
-        const float4 n1 = reinterpret_cast<const float4*>(vn + t0 + 8 * lg)[1];
-        const float4 s0 = reinterpret_cast<const float4*>(ks + t0 + 8 * lg)[0];
-        const float4 s1 = reinterpret_cast<const float4*>(ks + t0 + 8 * lg)[1];
-        float nn[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-        float ff[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const bool tail = t0 + kStep > te;
-        bool valid[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            valid[i] = !tail || (t0 + 8 * lg + i < te);
-            nn[i] = valid[i] ? nn[i] * nu : 0.0f;
-            ff[i] = valid[i] ? ff[i] * fs : 0.0f;
-        }
-        // ---- K -> fp16 A operands, S^T = K Q^T
-        f32x4 S[RT][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            half8 ka[KS];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                const uint4 v = kr[u][k / 2];
-                const uint32_t w0 = (k & 1) ? v.z : v.x;
-                const uint32_t w1 = (k & 1) ? v.w : v.y;
+                const uint4 v = kr[u * (DL / 16) + k / 2];
                 H8 h;
-                i8x4_to_h4(w0, h.u[0], h.u[1]);
-                i8x4_to_h4(w1, h.u[2], h.u[3]);
-                ka[k] = h.h;
+                i8x4_to_h4_offset((k & 1) ? v.z : v.x, h.u[0], h.u[1]);
+                i8x4_to_h4_offset((k & 1) ? v.w : v.y, h.u[2], h.u[3]);
+                ka[u][k] = h.h;
             }
+    };
+    // S^T of row tile rt for the step's 32 tokens: lane (lg, rl) gets tokens
+    // 8 lg + 4 u + j of row 16 rt + rl in S[u][j] (q . k for the int8 codes k)
+    auto scores = [&](const half8 (&ka)[2][KS], int rt, f32x4 (&S)[2]) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < 2; ++u) {
+            f32x4 sacc = {qoff[rt], qoff[rt], qoff[rt], qoff[rt]};
 #pragma unroll
-                for (int k = 0; k < KS; ++k) {
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qb[rt][k], s, 0, 0, 0);
-                    if constexpr (QSPLIT) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qlo[rt][k], s, 0, 0, 0);
+            for (int k = 0; k < KS; ++k) {
+                if constexpr (QSPLIT) {
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qreg[rt][k], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qlo[rt][k], sacc, 0, 0, 0);
+                } else {
+                    H8 q;
+                    q.v = g_qop[(rt * KS + k) * 64 + lane];
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], q.h, sacc, 0, 0, 0);
                 }
-                S[rt][u] = s;
             }
+            S[u] = sacc;
         }
-        // ---- scores (log2 units), lazy online softmax
-        float x[RT][8];
-        bool need = false;
+    };
+    auto norms = [&](const uint4 (&ns)[4], float (&nn)[8], float (&ff)[8]) {
+        const uint32_t w[16] = {ns[0].x, ns[0].y, ns[0].z, ns[0].w, ns[1].x, ns[1].y, ns[1].z, ns[1].w,
+                                ns[2].x, ns[2].y, ns[2].z, ns[2].w, ns[3].x, ns[3].y, ns[3].z, ns[3].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            nn[i] = __uint_as_float(w[i]);
+            ff[i] = __uint_as_float(w[8 + i]) * fs;  // Ks * sigma * log2 e: scores in log2 units
+        }
+    };
+
+    // Softmax reference per row: p = exp2(score - mref).  mref is fixed before the
+    // accumulation starts (this wavefront's first-step row max + kMargin), so the
+    // accumulators are never rescaled inside the loop (they stay in AGPRs, touched
+    // only by MFMAs).  The exponent also carries the weight scale nu = 2^lnu:
+    // x = score - mref + lnu, p' = 2^x = p * nu, w = p' * vn.  If a score exceeds
+    // mref + kLazy the weights could leave fp16 range: the workgroup then re-runs
+    // the unit with the exact row maxima as references.
+    float cref[RT], lsum[RT], xmax[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) cref[rt] = 0.0f;
+    if (my_steps > 0) {
+        wait_step(0);
+        half8 ka[2][KS];
+        Chunk<CB> ch;
+        uint4 ns[4];
+        read_slot(0, ka, ch, ns);
+        float nn[8], ff[8];
+        norms(ns, nn, ff);
+        const int t0 = tb + wave * kStep;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+            f32x4 S[2];
+            scores(ka, rt, S);
             float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float v = S[rt][i >> 2][i & 3] * ff[i];
-                v = valid[i] ? v : -INFINITY;
-                x[rt][i] = v;
-                mx = fmaxf(mx, v);
-            }
-            need |= mx > m[rt] + kLazy;
-            // stash the local max in lsum's neighbour slot via x[rt][*]: recomputed below if needed
+            for (int i = 0; i < 8; ++i)
+                if (t0 + 8 * lg + i < te) mx = fmaxf(mx, S[i >> 2][i & 3] * ff[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            cref[rt] = (float)lnu - (mx + kMargin);
         }
-        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) mx = fmaxf(mx, x[rt][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mnew = fmaxf(m[rt], mx);
-                const float alpha = (m[rt] == -INFINITY) ? 0.0f : exp2f(m[rt] - mnew);
-                lsum[rt] *= alpha;
-                m[rt] = mnew;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float aj = __shfl(alpha, 4 * lg + j, 64);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) acc[rt][nb][j] *= aj;
-                }
-            }
-        }
-        // weights w = p * vn * nu as fp16 hi + lo (w - hi rounded again): ~2^-22 relative
-        half8 Wh[RT], Wl[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const float mr = (m[rt] == -INFINITY) ? 0.0f : m[rt];
-            H8 wh, wl;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const float p0 = exp2f(x[rt][i] - mr);
-                const float p1 = exp2f(x[rt][i + 1] - mr);
-                lsum[rt] += p0 + p1;
-                const float w0 = p0 * nn[i], w1 = p1 * nn[i + 1];
-                const half2v hi = {(_Float16)w0, (_Float16)w1};
-                const half2v lo = {(_Float16)(w0 - (float)hi[0]), (_Float16)(w1 - (float)hi[1])};
-                wh.u[i / 2] = __builtin_bit_cast(uint32_t, hi);
-                wl.u[i / 2] = __builtin_bit_cast(uint32_t, lo);
-            }
-            Wh[rt] = wh.h;
-            Wl[rt] = wl.h;
-        }
-        // ---- acc += W x C  (C decoded per 16-dim column tile from the LUT)
-        pv_all<D, RT, BITS>(acc, Wh, Wl, ch, lut, lane_off);
     }
 
-    // ---- combine the 4 wavefronts in LDS (fixed order), write partial records
+    f32x4 acc[RT][NB];
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            lsum[rt] = 0.0f;
+            xmax[rt] = -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (pass == 1) {
+#pragma unroll
+            for (int it = 0; it < kStages - 1; ++it)
+                if (it < my_steps) issue(it);
+        }
+        // one 32-token step; TAIL masks tokens at or past the end of the split
+        auto step = [&](const int it, auto tail_tag) {
+            constexpr bool TAIL = decltype(tail_tag)::value;
+            const int t0 = tb + (wave + it * kWaves) * kStep;
+            if (it + kStages - 1 < my_steps) {
+                issue(it + kStages - 1);
+                wait_vmcnt<(kStages - 1) * SL::NDMA>();
+            } else {
+                wait_step(it);
+            }
+            half8 ka[2][KS];
+            Chunk<CB> ch;
+            uint4 ns[4];
+            read_slot(it, ka, ch, ns);
+            // V centroids for the 8 tokens x NB dims of this lane, from the LUT
+            half8 vb[NB];
+            decode_all<CB, BITS>(vb, ch, lutl);
+            float nn[8], ff[8];
+            norms(ns, nn, ff);
+            bool ok[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ok[i] = !TAIL || (t0 + 8 * lg + i < te);
+                if (TAIL) nn[i] = ok[i] ? nn[i] : 0.0f;
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 S[2];
+                scores(ka, rt, S);
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[i] = fmaf(S[i >> 2][i & 3], ff[i], cref[rt]);
+                    if (TAIL) x[i] = ok[i] ? x[i] : -INFINITY;
+                }
+                xmax[rt] = max3(max3(xmax[rt], x[0], x[1]), max3(x[2], x[3], x[4]), max3(x[5], x[6], x[7]));
+                // weights w = p' * vn as fp16 hi + lo (w - hi, rounded once more): ~2^-22 relative
+                H8 wh, wl;
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(x[i]);
+                    const float p1 = __builtin_amdgcn_exp2f(x[i + 1]);
+                    lsum[rt] += p0 + p1;
+                    const half2v hi = {(_Float16)(p0 * nn[i]), (_Float16)(p1 * nn[i + 1])};
+                    const half2v lo = {(_Float16)fmaf(p0, nn[i], -(float)hi[0]),
+                                       (_Float16)fmaf(p1, nn[i + 1], -(float)hi[1])};
+                    wh.u[i / 2] = __builtin_bit_cast(uint32_t, hi);
+                    wl.u[i / 2] = __builtin_bit_cast(uint32_t, lo);
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh.h, vb[nb], acc[rt][nb], 0, 0, 0);
+                    acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl.h, vb[nb], acc[rt][nb], 0, 0, 0);
+                }
+            }
+        };
+        // only the step holding the end of the split can be partial: it is the last
+        // step of one wavefront, run after the loop so the loop body has no masking
+        const bool has_tail = my_steps > 0 && (te - tb) % kStep != 0 && wave == (nsteps - 1) % kWaves;
+        const int full = my_steps - (has_tail ? 1 : 0);
+        for (int it = 0; it < full; ++it) step(it, std::false_type{});
+        if (has_tail) step(full, std::true_type{});
+        // any row over the limit? then every wave re-runs with the exact row maxima
+        if (tid == 0) g_flag = 0;
+        __syncthreads();
+        bool over = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float t = xmax[rt];
+            t = fmaxf(t, __shfl_xor(t, 16, 64));
+            t = fmaxf(t, __shfl_xor(t, 32, 64));
+            over |= t > (float)lnu + kLazy;
+            // this wave's max score of the row (log2 units)
+            if (lg == 0) g_m[wave][16 * rt + rl] = my_steps > 0 ? t - cref[rt] : -INFINITY;
+        }
+        if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(&g_flag, 1);
+        __syncthreads();
+        if (g_flag == 0) break;
+        // re-run reference: the exact row max over the workgroup (no score exceeds it)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, g_m[w][16 * rt + rl]);
+            cref[rt] = (float)lnu - M;
+        }
+        __syncthreads();
+    }
+    const float inv_nu = 1.0f / nu;
+    float m[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = my_steps > 0 ? (float)lnu - cref[rt] : -INFINITY;
+        lsum[rt] *= inv_nu;
+    }
+
+    // ---- combine the 4 wavefronts (fixed order, so results do not depend on timing)
+    constexpr int EPL = D / 64;
+    constexpr int RPW = kMaxRows / kWaves;  // rows finished per wavefront
+    const bool fused = a.fused != 0;
+    // fused finish with a suffix: fetch this wavefront's suffix records now, so their
+    // latency overlaps the combine (row = wave + kWaves * j)
+    float su_m[RPW], su_l[RPW], su_v[RPW][EPL];
+    if (fused && a.has_sfx) {
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + kWaves * j;
+            su_m[j] = -INFINITY;
+            su_l[j] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) su_v[j][e] = 0.0f;
+            if (row < R) {
+                const int k = P.agent0 + row / a.G;
+                const int head = g * a.G + row % a.G;
+                const float* ru = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + head) * (2 + D);
+                su_m[j] = ru[0];
+                su_l[j] = ru[1];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) su_v[j][e] = ru[2 + EPL * lane + e];
+            }
+        }
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         lsum[rt] += __shfl_xor(lsum[rt], 16, 64);
         lsum[rt] += __shfl_xor(lsum[rt], 32, 64);
         if (lg == 0) {
-            sm.m[wave][16 * rt + rl] = m[rt];
-            sm.l[wave][16 * rt + rl] = lsum[rt];
+            g_m[wave][16 * rt + rl] = m[rt];
+            g_l[wave][16 * rt + rl] = lsum[rt];
         }
     }
-    __syncthreads();  // also: every wave is done with the LUT
+    __syncthreads();  // every wave is done with the ring and the LUT
+    // this wave's tile: row 16 rt + 4 lg + j, dims NB * rl .. NB * rl + NB - 1
+    float* mine = g_big.accs + wave * (kMaxRows * D);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int row = 16 * rt + 4 * lg + j;
-            float M = -INFINITY;
+            float* dst = mine + (16 * rt + 4 * lg + j) * D + NB * rl;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][row]);
-            const float mw = sm.m[wave][row];
-            const float al = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[rt][nb][j] *= al;
+            for (int h = 0; h < NB / 4; ++h)
+                *reinterpret_cast<float4*>(dst + 4 * h) =
+                    make_float4(acc[rt][4 * h][j], acc[rt][4 * h + 1][j], acc[rt][4 * h + 2][j], acc[rt][4 * h + 3][j]);
         }
-    }
-    for (int w = 0; w < kWaves; ++w) {
-        if (wave == w) {
+    __syncthreads();
+    // row combine: M = max of the waves' references, weights 2^(m_w - M)
+    auto row_weights = [&](int row, float (&al)[kWaves], float& M, float& L) {
+        M = -INFINITY;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, g_m[w][row]);
+        L = 0.0f;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float* dst = &sm.accbuf[(16 * rt + 4 * lg + j) * D + NB * rl + nb];
-                        *dst = (w == 0) ? acc[rt][nb][j] : *dst + acc[rt][nb][j];
-                    }
-        }
-        __syncthreads();
-    }
-    const float inv_nu = 1.0f / nu;
-    float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.splits + sp) * (uint64_t)R * (2 + D);
-    for (int idx = tid; idx < R * D; idx += 256) {
-        const int row = idx / D, i = idx % D;
-        rec0[(uint64_t)row * (2 + D) + 2 + i] = sm.accbuf[row * D + i] * inv_nu;
-    }
-    for (int row = tid; row < R; row += 256) {
-        float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][row]);
-        float Lr = 0.0f;
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = sm.m[w][row];
-            Lr += (mw == -INFINITY) ? 0.0f : exp2f(mw - M) * sm.l[w][row];
+            const float mw = g_m[w][row];
+            al[w] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+            L += al[w] * g_l[w][row];
         }
-        rec0[(uint64_t)row * (2 + D)] = M;
-        rec0[(uint64_t)row * (2 + D) + 1] = Lr;
+    };
+    if (!fused) {
+        float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.splits + sp) * (uint64_t)R * (2 + D);
+        for (int row = wave; row < R; row += kWaves) {
+            float al[kWaves], M, L;
+            row_weights(row, al, M, L);
+            float* rec = rec0 + (uint64_t)row * (2 + D);
+            for (int i = lane; i < D; i += 64) {
+                float z = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) z += al[w] * g_big.accs[w * (kMaxRows * D) + row * D + i];
+                rec[2 + i] = z * inv_nu;
+            }
+            if (lane == 0) {
+                rec[0] = M;
+                rec[1] = L;
+            }
+        }
+        return;
+    }
+    // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int row = wave + kWaves * j;
+        if (row >= R) break;
+        float al[kWaves], M, L;
+        row_weights(row, al, M, L);
+        float z[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float* src = g_big.accs + w * (kMaxRows * D) + row * D + EPL * lane;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) z[e] += al[w] * src[e];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) z[e] *= inv_nu;
+        // inverse rotation: unnormalised Hadamard over the D values (in-lane stage
+        // first, then lane distance 1 .. 32), divided by D below
+        if (EPL == 2) {
+            const float u0 = z[0], u1 = z[EPL - 1];
+            z[0] = u0 + u1;
+            z[EPL - 1] = u0 - u1;
+        }
+        auto stage = [&](auto off_tag) {
+            constexpr int OFF = decltype(off_tag)::value;
+            const float sg = (lane & OFF) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) z[e] = fmaf(sg, z[e], lane_xor<OFF>(z[e]));
+        };
+        stage(std::integral_constant<int, 1>{});
+        stage(std::integral_constant<int, 2>{});
+        stage(std::integral_constant<int, 4>{});
+        stage(std::integral_constant<int, 8>{});
+        stage(std::integral_constant<int, 16>{});
+        stage(std::integral_constant<int, 32>{});
+        const int k = P.agent0 + row / a.G;
+        const int head = g * a.G + row % a.G;
+        float o[EPL];
+        float denom;
+        if (a.has_sfx) {
+            const float mu = su_m[j];
+            const float M2 = fmaxf(M, mu);
+            const float ap = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
+            const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
+            denom = ap * L + au * su_l[j];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = ap * z[e] * (1.0f / D) + au * su_v[j][e];
+        } else {
+            denom = L;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = z[e] * (1.0f / D);
+        }
+        const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
+        float* out = a.out + (((uint64_t)a.agent_id[k] * a.lc + lj) * a.hq + head) * D + EPL * lane;
+        if constexpr (EPL == 2) {
+            *reinterpret_cast<float2*>(out) = make_float2(o[0] * rinv, o[1] * rinv);
+        } else {
+            out[0] = o[0] * rinv;
+        }
     }
 }
 
 template <int D, int RT, bool QSPLIT>
 __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents) {
-    __shared__ Smem sm;
     const PoolEntry& P = a.pools[find_pool_m(a, blockIdx.x)];
     int local = blockIdx.x - P.wg_begin;
     local /= P.splits;
     const int l = a.l0 + local / a.hkv;
     switch (layer_bits(P, l)) {
-        case 2: pool_mfma_body<D, RT, 2, QSPLIT>(a, cents, sm); break;
-        case 3: pool_mfma_body<D, RT, 3, QSPLIT>(a, cents, sm); break;
-        default: pool_mfma_body<D, RT, 4, QSPLIT>(a, cents, sm); break;
+        case 2: pool_mfma_body<D, RT, 2, QSPLIT>(a, cents); break;
+        case 3: pool_mfma_body<D, RT, 3, QSPLIT>(a, cents); break;
+        default: pool_mfma_body<D, RT, 4, QSPLIT>(a, cents); break;
     }
 }
 
@@ -455,7 +780,11 @@ int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int
         case 1: hipLaunchKernelGGL((k_pool_mfma<D, 1, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
         case 2: hipLaunchKernelGGL((k_pool_mfma<D, 2, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
         case 3: hipLaunchKernelGGL((k_pool_mfma<D, 3, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
-        default: hipLaunchKernelGGL((k_pool_mfma<D, 4, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
+        default:
+            // split fp32 queries hold two operand sets in registers: at most 48 rows
+            if constexpr (QSPLIT) return PKV_EUNSUPPORTED;
+            else hipLaunchKernelGGL((k_pool_mfma<D, 4, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c);
+            break;
     }
     return PKV_OK;
 }
@@ -463,8 +792,9 @@ int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int
 }  // namespace
 
 bool mfma_supported(const DecodeLaunch& a) {
+    const int limit = a.q_dtype == PKV_F32 ? 48 : 64;
     for (int p = 0; p < a.n_pools; ++p)
-        if (a.pools[p].rows > 64) return false;
+        if (a.pools[p].rows > limit) return false;
     return true;
 }
 

@@ -10,16 +10,18 @@
 // Three launches per append, all on the caller's stream:
 //   1. k_reset      clear the per-layer amax scratch (and Vmax on a fresh layer)
 //   2. k_amax       max |k| per layer, reduced with an atomic max on fp32 bits
-//   3. k_encode     one wavefront per 8-token code group of one (layer, kv head):
-//                   int8 K rows, then per token an in-register FWHT across the
-//                   wave (head_dim 64: one element per lane; 128: two), the
-//                   norm by a fixed halving tree, and the code search; the
-//                   wave collects the group's code fields and stores them.
+//   3. k_encode     a wavefront encodes one 8-token code group of one (layer,
+//                   kv head) at a time: int8 K rows, then for the 8 tokens
+//                   together an in-register FWHT across the wave (head_dim 64:
+//                   one element per lane; 128: two), the norm by a fixed
+//                   halving tree, and the code search; the group's code fields
+//                   are staged in LDS and stored as dwords.
 // Every floating-point step uses one IEEE rounding (no FMA contraction, correctly
 // rounded division and square root), so codes are reproducible bit for bit.
 #include <cstring>
 
 #include "pkv_internal.h"
+#include "pkv_lanes.h"
 
 namespace pkv {
 namespace {
@@ -60,35 +62,62 @@ __global__ void k_reset(EncodeArgs a) {
     }
 }
 
-// grid (blocks per layer, nl), 256 threads
+// grid (kAmaxBlocks, nl), 256 threads.  Few blocks per layer keep the number of
+// same-address atomics small (the per-layer maxima share one cache line).
+constexpr int kAmaxBlocks = 16;
+
 __global__ void __launch_bounds__(256) k_amax(EncodeArgs a) {
     const int j = blockIdx.y;
     const uint64_t per_layer = (uint64_t)a.hkv * a.n * a.d;
     const uint64_t base = (uint64_t)j * per_layer;
-    float m = 0.0f;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    float m0 = 0.0f, m1 = 0.0f;
     if (a.dtype == PKV_BF16) {
         // 8 bf16 per 16-byte load; per_layer and base are multiples of 64 elements
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + base);
         const uint64_t nv = per_layer / 8;
-        for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv;
-             i += (uint64_t)gridDim.x * blockDim.x) {
+        uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        for (; i + 3 * stride < nv; i += 4 * stride) {
+            uint4 w[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = p[i + r * stride];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t u[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    m0 = fmaxf(m0, fabsf(__uint_as_float(u[e] << 16)));
+                    m1 = fmaxf(m1, fabsf(__uint_as_float(u[e] & 0xffff0000u)));
+                }
+            }
+        }
+        for (; i < nv; i += stride) {
             const uint4 w = p[i];
             const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                m = fmaxf(m, fabsf(__uint_as_float(u[e] << 16)));
-                m = fmaxf(m, fabsf(__uint_as_float(u[e] & 0xffff0000u)));
+                m0 = fmaxf(m0, fabsf(__uint_as_float(u[e] << 16)));
+                m1 = fmaxf(m1, fabsf(__uint_as_float(u[e] & 0xffff0000u)));
             }
         }
     } else {
         const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + base);
         const uint64_t nv = per_layer / 4;
-        for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv;
-             i += (uint64_t)gridDim.x * blockDim.x) {
+        uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        for (; i + 3 * stride < nv; i += 4 * stride) {
+            float4 w[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = p[i + r * stride];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                m0 = fmaxf(fmaxf(m0, fabsf(w[r].x)), fmaxf(fabsf(w[r].y), fmaxf(fabsf(w[r].z), fabsf(w[r].w))));
+        }
+        for (; i < nv; i += stride) {
             const float4 w = p[i];
-            m = fmaxf(fmaxf(m, fabsf(w.x)), fmaxf(fabsf(w.y), fmaxf(fabsf(w.z), fabsf(w.w))));
+            m1 = fmaxf(fmaxf(m1, fabsf(w.x)), fmaxf(fabsf(w.y), fmaxf(fabsf(w.z), fabsf(w.w))));
         }
     }
+    float m = fmaxf(m0, m1);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     __shared__ float wmax[4];
@@ -102,133 +131,200 @@ __global__ void __launch_bounds__(256) k_amax(EncodeArgs a) {
     }
 }
 
-// One wavefront per (group, kv head, layer); EPL = head_dim / 64 elements per lane.
-// Lane lam holds dimensions EPL*lam .. EPL*lam + EPL-1.
-template <int EPL>
-__device__ void encode_group(const EncodeArgs& a, int grp, int g, int j) {
+constexpr int kEncWaves = 4;
+constexpr int kGroupsPerWg = 64;  // 512 tokens per workgroup: one Vmax atomic per workgroup
+
+// One level of the halving-tree sum of squares across lanes: s <- s + s[lane ^ M].
+template <int M, int EPL>
+__device__ __forceinline__ void tree_level(float (&sq)[kGroupTokens][EPL]) {
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sq[i][e] = sq[i][e] + lane_xor<M>(sq[i][e]);
+}
+
+// One FWHT stage across lanes: the lane with bit M clear keeps z + p, the one with
+// it set gets p - z (p = partner's z); fma(+-1, z, p) is exactly that sum.
+template <int M, int EPL>
+__device__ __forceinline__ void butterfly(float (&z)[kGroupTokens][EPL], int lane) {
+    const float sgn = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) z[i][e] = __builtin_fmaf(sgn, z[i][e], lane_xor<M>(z[i][e]));
+}
+
+// One wavefront encodes one 8-token code group of one (layer, kv head); the 8
+// tokens are processed together so their cross-lane reductions and butterflies
+// are independent and overlap.  Lane lam holds dimensions EPL*lam .. EPL*lam + EPL-1.
+template <int EPL, int BITS>
+__device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t* stage, float& nmax) {
 #pragma clang fp contract(off)
     constexpr int D = 64 * EPL;
+    constexpr int NT = (1 << BITS) - 1;
     const int lane = threadIdx.x & 63;
     const int l = a.l0 + j;
-    const int b = a.bits[j];
-    const int nthr = (1 << b) - 1;
-    const float* thr = a.thr[b - 2];
+    const float* thr = a.thr[BITS - 2];
 
     const float amax = __uint_as_float(reinterpret_cast<const uint32_t*>(a.base + a.off_amax)[l]);
     const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
 
     const int gt0 = grp * kGroupTokens;
-    const int tb = max(a.t0, gt0);
-    const int te = min(a.t0 + a.n, gt0 + kGroupTokens);
-
-    uint8_t* vc = a.base + a.off_vc[j] + ((uint64_t)g * (a.tc / kGroupTokens) + grp) * (uint64_t)(D * b);
-    uint32_t field[EPL];
+    bool valid[kGroupTokens];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        field[e] = 0u;
-        if (gt0 < a.t0) {  // first group of an append that starts mid-group: keep earlier tokens
-            const int dim = EPL * lane + e;
-            uint32_t old = 0u;
-            for (int k = 0; k < b; ++k) old |= static_cast<uint32_t>(vc[dim * b + k]) << (8 * k);
-            field[e] = old & ((1u << (b * (a.t0 - gt0))) - 1u);
-        }
-    }
+    for (int i = 0; i < kGroupTokens; ++i) valid[i] = gt0 + i >= a.t0 && gt0 + i < a.t0 + a.n;
 
-    int8_t* kq = reinterpret_cast<int8_t*>(a.base + a.off_kq) + ((uint64_t)l * a.hkv + g) * a.tc * D;
-    float* vn = reinterpret_cast<float*>(a.base + a.off_vn) + ((uint64_t)l * a.hkv + g) * a.tc;
-    float* ks = reinterpret_cast<float*>(a.base + a.off_ks) + (uint64_t)l * a.tc;
-    float nmax = 0.0f;
-
-    for (int t = tb; t < te; ++t) {
-        const uint64_t src = (((uint64_t)j * a.hkv + g) * a.n + (t - a.t0)) * D + EPL * lane;
-        // ---- K row: q = clamp(rint(k / s), -127, 127)
-        int8_t qv[EPL];
+    // ---- loads (K and V of the group's tokens in this append)
+    float kx[kGroupTokens][EPL], vx[kGroupTokens][EPL];
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        const uint64_t src = (((uint64_t)j * a.hkv + g) * a.n + (valid[i] ? gt0 + i - a.t0 : 0)) * D + EPL * lane;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const float x = load_elem(a.k, a.dtype, src + e);
+            kx[i][e] = valid[i] ? load_elem(a.k, a.dtype, src + e) : 0.0f;
+            vx[i][e] = valid[i] ? load_elem(a.v, a.dtype, src + e) : 0.0f;
+        }
+    }
+    // ---- K rows: q = clamp(rint(k / s), -127, 127)
+    int8_t* kq = reinterpret_cast<int8_t*>(a.base + a.off_kq) + ((uint64_t)l * a.hkv + g) * a.tc * D;
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        if (!valid[i]) continue;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
             float q = 0.0f;
-            if (s > 0.0f) q = fminf(fmaxf(rintf(x / s), -127.0f), 127.0f);
-            qv[e] = static_cast<int8_t>(static_cast<int>(q));
+            if (s > 0.0f) q = fminf(fmaxf(rintf(kx[i][e] / s), -127.0f), 127.0f);
+            packed |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(static_cast<int>(q)))) << (8 * e);
         }
-        if (EPL == 2) {
-            const uint16_t pair = static_cast<uint16_t>(static_cast<uint8_t>(qv[0])) |
-                                  static_cast<uint16_t>(static_cast<uint16_t>(static_cast<uint8_t>(qv[EPL - 1])) << 8);
-            reinterpret_cast<uint16_t*>(kq + (uint64_t)t * D)[lane] = pair;
-        } else {
-            kq[(uint64_t)t * D + lane] = qv[0];
-        }
-        // ---- V vector
-        float x[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = load_elem(a.v, a.dtype, src + e);
-        // sum of squares: halving tree, element i pairs with i + h for h = D/2 .. 1
-        float sq[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sq[e] = x[e] * x[e];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) sq[e] = sq[e] + __shfl_xor(sq[e], off, 64);
-        }
-        float ss = sq[0];
-        if (EPL == 2) ss = sq[0] + sq[EPL - 1];
-        const float nrm = sqrtf(ss);
-        // FWHT, ascending half-width h: in-lane stage first when EPL == 2
-        float z[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) z[e] = x[e];
-        if (EPL == 2) {
-            const float u = z[0], w = z[EPL - 1];
-            z[0] = u + w;
-            z[EPL - 1] = u - w;
-        }
-#pragma unroll
-        for (int off = 1; off <= 32; off <<= 1) {
-            const bool upper = (lane & off) != 0;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float p = __shfl_xor(z[e], off, 64);
-                z[e] = upper ? (p - z[e]) : (z[e] + p);
-            }
-        }
-        // codes: number of thresholds strictly below y = z * (1/n)
-        if (nrm > 0.0f) {
-            const float r = 1.0f / nrm;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float y = z[e] * r;
-                uint32_t c = 0;
-                for (int k = 0; k < nthr; ++k) c += (y > thr[k]) ? 1u : 0u;
-                field[e] |= c << (b * (t - gt0));
-            }
-        }
-        if (lane == 0) {
-            vn[t] = nrm;
-            if (g == 0) ks[t] = s;
-        }
-        nmax = fmaxf(nmax, nrm);
+        if (EPL == 2)
+            reinterpret_cast<uint16_t*>(kq + (uint64_t)(gt0 + i) * D)[lane] = static_cast<uint16_t>(packed);
+        else
+            kq[(uint64_t)(gt0 + i) * D + lane] = static_cast<int8_t>(packed);
     }
-    // store this lane's code fields: dimension dim -> bytes [dim*b, dim*b + b)
+    // ---- V: sum of squares by the halving tree (element i pairs with i + h, h = D/2 .. 1)
+    float sq[kGroupTokens][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int dim = EPL * lane + e;
-        for (int k = 0; k < b; ++k) vc[dim * b + k] = static_cast<uint8_t>(field[e] >> (8 * k));
+    for (int i = 0; i < kGroupTokens; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sq[i][e] = vx[i][e] * vx[i][e];
+    tree_level<32>(sq);
+    tree_level<16>(sq);
+    tree_level<8>(sq);
+    tree_level<4>(sq);
+    tree_level<2>(sq);
+    tree_level<1>(sq);
+    float nrm[kGroupTokens];
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        float ss = sq[i][0];
+        if (EPL == 2) ss = sq[i][0] + sq[i][EPL - 1];
+        nrm[i] = sqrtf(ss);
     }
-    if (lane == 0 && te > tb) {
+    // ---- FWHT, ascending half-width (the in-lane stage first when EPL == 2)
+    if (EPL == 2) {
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i) {
+            const float u = vx[i][0], w = vx[i][EPL - 1];
+            vx[i][0] = u + w;
+            vx[i][EPL - 1] = u - w;
+        }
+    }
+    butterfly<1>(vx, lane);
+    butterfly<2>(vx, lane);
+    butterfly<4>(vx, lane);
+    butterfly<8>(vx, lane);
+    butterfly<16>(vx, lane);
+    butterfly<32>(vx, lane);
+    // ---- codes: number of thresholds strictly below y = z * (1/n); 8 tokens per field
+    uint32_t field[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) field[e] = 0u;
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        if (!valid[i] || !(nrm[i] > 0.0f)) continue;
+        const float r = 1.0f / nrm[i];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float y = vx[i][e] * r;
+            uint32_t c = 0;
+#pragma unroll
+            for (int k = 0; k < NT; ++k) c += (y > thr[k]) ? 1u : 0u;
+            field[e] |= c << (BITS * i);
+        }
+        nmax = fmaxf(nmax, nrm[i]);
+    }
+    uint8_t* vc = a.base + a.off_vc[j] + ((uint64_t)g * (a.tc / kGroupTokens) + grp) * (uint64_t)(D * BITS);
+    if (gt0 < a.t0) {  // the append starts inside this group: keep the earlier tokens' bits
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int dim = EPL * lane + e;
+            uint32_t old = 0u;
+#pragma unroll
+            for (int k = 0; k < BITS; ++k) old |= static_cast<uint32_t>(vc[dim * BITS + k]) << (8 * k);
+            field[e] |= old & ((1u << (BITS * (a.t0 - gt0))) - 1u);
+        }
+    }
+    // ---- norms and scales of the valid tokens: lane i < 8 stores token i
+    float* vn = reinterpret_cast<float*>(a.base + a.off_vn) + ((uint64_t)l * a.hkv + g) * a.tc;
+    float* ks = reinterpret_cast<float*>(a.base + a.off_ks) + (uint64_t)l * a.tc;
+    float mine = 0.0f;
+    bool mine_ok = false;
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i)
+        if (lane == i) {
+            mine = nrm[i];
+            mine_ok = valid[i];
+        }
+    if (lane < kGroupTokens && mine_ok) {
+        vn[gt0 + lane] = mine;
+        if (g == 0) ks[gt0 + lane] = s;
+    }
+    // ---- code fields: dimension dim -> bytes [dim*BITS, dim*BITS + BITS), staged in LDS
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) stage[(EPL * lane + e) * BITS + k] = static_cast<uint8_t>(field[e] >> (8 * k));
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    constexpr int NW = D * BITS / 4;  // dwords of the group
+    for (int w = lane; w < NW; w += 64)
+        reinterpret_cast<uint32_t*>(vc)[w] = reinterpret_cast<const uint32_t*>(stage)[w];
+    __builtin_amdgcn_wave_barrier();
+}
+
+// grid (ceil(groups / kGroupsPerWg), hkv, nl), 256 threads
+template <int EPL, int BITS>
+__device__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
+    __shared__ __align__(16) uint8_t stage[kEncWaves][128 * 4];
+    __shared__ float wmax[kEncWaves];
+    const int wave = threadIdx.x >> 6;
+    const int g = blockIdx.y, j = blockIdx.z;
+    float nmax = 0.0f;
+    const int gb = blockIdx.x * kGroupsPerWg;
+    const int ge = min(n_grp, gb + kGroupsPerWg);
+    for (int gi = gb + wave; gi < ge; gi += kEncWaves)
+        encode_group<EPL, BITS>(a, grp_first + gi, g, j, stage[wave], nmax);
+    if ((threadIdx.x & 63) == 0) wmax[wave] = nmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float r = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         float* vmax = reinterpret_cast<float*>(a.base + a.off_vmax);
-        atomicMax(reinterpret_cast<uint32_t*>(vmax + (uint64_t)l * a.hkv + g), __float_as_uint(nmax));
+        atomicMax(reinterpret_cast<uint32_t*>(vmax + (uint64_t)(a.l0 + j) * a.hkv + g), __float_as_uint(r));
     }
 }
 
-// grid (ceil(groups / 4), hkv, nl), 256 threads = 4 wavefronts, one group each
 __global__ void __launch_bounds__(256) k_encode(EncodeArgs a, int grp_first, int n_grp) {
-    const int wave = threadIdx.x >> 6;
-    const int gi = blockIdx.x * 4 + wave;
-    if (gi >= n_grp) return;
-    if (a.d == 128)
-        encode_group<2>(a, grp_first + gi, blockIdx.y, blockIdx.z);
-    else
-        encode_group<1>(a, grp_first + gi, blockIdx.y, blockIdx.z);
+    const int b = a.bits[blockIdx.z];
+    if (a.d == 128) {
+        if (b == 2) encode_wg<2, 2>(a, grp_first, n_grp);
+        else if (b == 3) encode_wg<2, 3>(a, grp_first, n_grp);
+        else encode_wg<2, 4>(a, grp_first, n_grp);
+    } else {
+        if (b == 2) encode_wg<1, 2>(a, grp_first, n_grp);
+        else if (b == 3) encode_wg<1, 3>(a, grp_first, n_grp);
+        else encode_wg<1, 4>(a, grp_first, n_grp);
+    }
 }
 
 }  // namespace
@@ -279,16 +375,12 @@ extern "C" int pool_quantize_append(pkv_pool* pool, int32_t layer_begin, int32_t
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(k_reset, dim3(layer_count), dim3(64), 0, s, a);
-    const uint64_t per_layer = (uint64_t)c.n_kv_heads * n_tokens * c.head_dim;
-    const uint64_t vecs = per_layer / 8;
-    unsigned blocks = (unsigned)std::min<uint64_t>(1024, (vecs + 255) / 256);
-    if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(k_amax, dim3(blocks, layer_count), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_amax, dim3(kAmaxBlocks, layer_count), dim3(256), 0, s, a);
     const int grp_first = t0 / kGroupTokens;
     const int grp_last = (t0 + n_tokens - 1) / kGroupTokens;
     const int n_grp = grp_last - grp_first + 1;
-    hipLaunchKernelGGL(k_encode, dim3((n_grp + 3) / 4, c.n_kv_heads, layer_count), dim3(256), 0, s, a,
-                       grp_first, n_grp);
+    hipLaunchKernelGGL(k_encode, dim3((n_grp + kGroupsPerWg - 1) / kGroupsPerWg, c.n_kv_heads, layer_count),
+                       dim3(256), 0, s, a, grp_first, n_grp);
     const int st = launch_status();
     if (st != PKV_OK) return st;
     for (int l = layer_begin; l < layer_begin + layer_count; ++l) pool->n_tokens[l] = t0 + n_tokens;

@@ -125,6 +125,9 @@ DECODE_CASES = {
     "g8_rows_over_32": (wl.QWEN3_32B_MIXED.replace(n_layers=1, n_q_heads=16, n_kv_heads=2, pool_tokens=64,
                                                    sfx_tokens=8, n_agents=5, n_pools=1, v_bits_mode="uniform3"),
                         1, [8, 0, 3, 8, 1], False),
+    "g16_two_suffix_passes": (wl.LLAMA3_8B.replace(n_layers=1, n_q_heads=32, n_kv_heads=2, pool_tokens=130,
+                                                   sfx_tokens=70), 1, [70, 65], False),
+    "tiny_fp32_with_suffix": (wl.TINY.replace(sfx_tokens=40, sfx_mode="fixed"), 1, [40, 0, 7, 33], False),
 }
 
 
@@ -178,6 +181,45 @@ def test_decode_is_deterministic_and_batch_independent(kernel):
     solo = h.run_decode([dp.pool], q[1:2].contiguous(), (kd[1:2].contiguous(), vd[1:2].contiguous()), [8],
                         kernel=kernel)
     assert np.max(np.abs(solo[0] - a[1])) <= 1e-6 * max(1.0, np.max(np.abs(a[1])))
+
+
+def _ramp_pool(h, slope, T=300, Hkv=2, d=128, seed=5):
+    """A pool whose keys grow (slope > 0) or shrink along the tokens in one direction u."""
+    rng = np.random.default_rng(seed)
+    u = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    ramp = np.arange(T, dtype=np.float64) / T
+    base = ramp if slope > 0 else 1.0 - ramp
+    k = (abs(slope) * base[None, :, None] * u[None, None, :]
+         + 0.1 * rng.standard_normal((Hkv, T, d)))[None].astype(np.float32)
+    v = rng.standard_normal((1, Hkv, T, d)).astype(np.float32)
+    dp = h.DevicePool(1, Hkv, d, T, [3])
+    ref = pool_image.PoolImage(1, Hkv, d, T, [3])
+    ref.append(0, k, v)
+    dp.append(0, torch.from_numpy(k).to(h.DEV), torch.from_numpy(v).to(h.DEV))
+    return dp, ref, u
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("qdtype", ["bf16", "f32"])
+@pytest.mark.parametrize("slope", [2.0, -2.0])
+def test_decode_scores_far_from_first_tokens(kernel, qdtype, slope):
+    # Scores that rise by ~65 log2 units along the pool (slope > 0: far above any
+    # reference taken from the first tokens) or fall from them (slope < 0); rows of
+    # one kv head mix agents whose queries point along +u, -u and half of +u.
+    h = H()
+    print(f"[decode] ramp slope={slope} q={qdtype} kernel={kernel}", flush=True)
+    dp, ref, u = _ramp_pool(h, slope)
+    G, A = 4, 3
+    scale = np.array([2.0, -2.0, 1.0])
+    q32 = (scale[:, None, None, None] * np.broadcast_to(u, (A, 1, 2 * G, 128))).astype(np.float32)
+    q = torch.from_numpy(np.ascontiguousarray(q32)).to(h.DEV)
+    if qdtype == "bf16":
+        q = q.to(torch.bfloat16)  # +-2, +-1: exact in bf16
+    for splits in (0, 3):
+        out = h.run_decode([dp.pool] * A, q, kernel=kernel, splits=splits)
+        exp = h.oracle_decode(q32.astype(np.float64), [0] * A, [ref], None, None, [0] * A, 2)
+        err = attention.max_rel_error(out, exp)
+        assert err <= TOL, (splits, err)
 
 
 def test_zero_agents_is_a_no_op():
