@@ -180,7 +180,8 @@ typedef struct {
  * *workspace_bytes (nothing enqueued); PKV_ENOSPACE if the given size is too
  * small.  The size depends only on the call's shapes and the split plan.
  * All agents' pools must share n_kv_heads and head_dim, hold the layers of the
- * call, and hold the same token count in each of those layers.
+ * call, and hold the same token count in each of those layers.  q, out,
+ * sfx_k and sfx_v must be 16-byte aligned (PKV_EINVAL otherwise).
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOSPACE, PKV_EHIP.
  */
 int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,

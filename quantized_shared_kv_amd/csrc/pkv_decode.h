@@ -25,6 +25,8 @@ struct PoolEntry {
     int32_t chunk;         // tokens per split (multiple of 32)
     int32_t rblocks;       // row blocks per (layer, kv head, split)
     int32_t wg_begin;      // first workgroup of this pool in the launch
+    int32_t agent_base;    // >= 0: the pool's launch agents agent0 + i are call agents
+                           // agent_base + i (no table lookup needed); -1 otherwise
 };
 
 struct DecodeLaunch {

@@ -591,6 +591,9 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.part_off = part;
             part += (uint64_t)units * e.splits * e.rows * record_floats(d);
             wg += units * e.splits * e.rblocks;
+            e.agent_base = c.agents[0];
+            for (size_t i = 0; i < c.agents.size(); ++i)
+                if (c.agents[i] != c.agents[0] + (int)i) e.agent_base = -1;
             for (size_t i = 0; i < c.agents.size(); ++i) {
                 const int a = c.agents[i];
                 L.agent_id[n_agents] = (int16_t)a;
@@ -622,6 +625,9 @@ int validate(const pkv_decode_args* x) {
     if (x->n_agents == 0 || x->layer_count == 0) return PKV_OK;
     if (x->n_agents > 32767) return PKV_EINVAL;
     if (!x->agent_pool || !x->q || !x->out) return PKV_EINVAL;
+    // the kernels read and write whole 16-byte chunks of these arrays
+    auto misaligned = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+    if (misaligned(x->q) || misaligned(x->out) || misaligned(x->sfx_k) || misaligned(x->sfx_v)) return PKV_EINVAL;
     if (x->q_dtype != PKV_F32 && x->q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
     if (x->kernel < 0 || x->kernel > PKV_KERNEL_MFMA || x->splits < 0) return PKV_EINVAL;
     if (!(x->softmax_scale >= 0.0f) || std::isinf(x->softmax_scale)) return PKV_EINVAL;

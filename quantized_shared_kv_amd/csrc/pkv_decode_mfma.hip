@@ -343,7 +343,34 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         dma<4>(nsrc, st + SL::NOFF);
     };
 
-    // start the ring (kStages - 1 steps ahead) first, so the loads overlap the set-up
+    // ---- set-up loads first, all at once: this lane's query chunks (8 values per
+    // (row tile, k-step): one 16-byte load for bf16, two for fp32) and one codebook
+    // entry per lane; then the ring, so that waiting for the set-up loads does not
+    // wait for the ring
+    constexpr int QV = QSPLIT ? 2 : 1;
+    uint4 qraw[RT][KS][QV];
+    bool rok[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int rho = 16 * rt + rl;
+        rok[rt] = rho < R;
+        const int rr = rok[rt] ? rho : 0;
+        const int agent = P.agent_base >= 0 ? P.agent_base + rr / a.G : a.agent_id[P.agent0 + rr / a.G];
+        const int head = g * a.G + rr % a.G;
+        const uint64_t qo = (((uint64_t)agent * a.lc + lj) * a.hq + head) * D + lg * DL;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            if constexpr (QSPLIT) {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qo + 8 * k);
+                qraw[rt][k][0] = src[0];
+                qraw[rt][k][QV - 1] = src[1];
+            } else {
+                qraw[rt][k][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + 8 * k);
+            }
+        }
+    }
+    const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x
+
 #pragma unroll
     for (int it = 0; it < kStages - 1; ++it)
         if (it < my_steps) issue(it);
@@ -356,31 +383,28 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     float qoff[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int rho = 16 * rt + rl;
-        const bool ok = rho < R;
-        const int rr = ok ? rho : 0;
-        const int agent = a.agent_id[P.agent0 + rr / a.G];
-        const int head = g * a.G + rr % a.G;
-        const uint64_t qo = (((uint64_t)agent * a.lc + lj) * a.hq + head) * D + lg * DL;
         float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
+            uint32_t w[8];
+            if constexpr (QSPLIT) {
+                const uint4 r0 = qraw[rt][k][0], r1 = qraw[rt][k][QV - 1];
+                w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
+                w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
+            } else {
+                const uint4 r0 = qraw[rt][k][0];
+                const uint32_t h[4] = {r0.x, r0.y, r0.z, r0.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w[2 * i] = h[i] << 16;              // bf16 -> fp32 bits
+                    w[2 * i + 1] = h[i] & 0xffff0000u;
+                }
+            }
             H8 hv, lv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x0 = 0.0f, x1 = 0.0f;
-                if (ok) {
-                    if (a.q_dtype == PKV_BF16) {
-                        const uint32_t two = reinterpret_cast<const uint32_t*>(
-                            static_cast<const uint16_t*>(a.q) + qo + 8 * k)[i];
-                        x0 = __uint_as_float(two << 16);
-                        x1 = __uint_as_float(two & 0xffff0000u);
-                    } else {
-                        const float2 two = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qo + 8 * k)[i];
-                        x0 = two.x;
-                        x1 = two.y;
-                    }
-                }
+                const float x0 = rok[rt] ? __uint_as_float(w[2 * i]) : 0.0f;
+                const float x1 = rok[rt] ? __uint_as_float(w[2 * i + 1]) : 0.0f;
                 hv.u[i] = pack_h2(x0, x1);
                 const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
                 sum += (float)hh[0] + (float)hh[1];
@@ -404,11 +428,13 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
     // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
     {
-        const float* c = cents.c[BITS - 2];
         constexpr int NE = 1 << (2 * BITS);
-        for (int i = tid; i < NE * kLutCopies; i += 256) {
-            const int e = i / kLutCopies;
-            g_big.loop.lut[i] = pack_h2(c[e & ((1 << BITS) - 1)], c[e >> BITS]);
+#pragma unroll
+        for (int i0 = 0; i0 < NE * kLutCopies; i0 += 256) {
+            const int e = (i0 + tid) / kLutCopies;
+            const float c0 = __shfl(cl, e & ((1 << BITS) - 1), 64);
+            const float c1 = __shfl(cl, e >> BITS, 64);
+            g_big.loop.lut[i0 + tid] = pack_h2(c0, c1);
         }
     }
     __syncthreads();  // LUT and query operands ready
@@ -623,6 +649,12 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // fused finish with a suffix: fetch this wavefront's suffix records now, so their
     // latency overlaps the combine (row = wave + kWaves * j)
     float su_m[RPW], su_l[RPW], su_v[RPW][EPL];
+    int out_agent[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int row = min(wave + kWaves * j, R - 1);
+        out_agent[j] = P.agent_base >= 0 ? P.agent_base + row / a.G : a.agent_id[P.agent0 + row / a.G];
+    }
     if (fused && a.has_sfx) {
 #pragma unroll
         for (int j = 0; j < RPW; ++j) {
@@ -697,36 +729,43 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
         return;
     }
-    // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store
+    // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store;
+    // four rows at a time so their lane exchanges overlap
+    constexpr int RB = 4;
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int row = wave + kWaves * j;
-        if (row >= R) break;
-        float al[kWaves], M, L;
-        row_weights(row, al, M, L);
-        float z[EPL];
+    for (int j0 = 0; j0 < RPW; j0 += RB) {
+        if (wave + kWaves * j0 >= R) break;
+        float z[RB][EPL], M[RB], L[RB];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
+        for (int jj = 0; jj < RB; ++jj) {
+            const int row = min(wave + kWaves * (j0 + jj), R - 1);  // rows past R: computed, not stored
+            float al[kWaves];
+            row_weights(row, al, M[jj], L[jj]);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float* src = g_big.accs + w * (kMaxRows * D) + row * D + EPL * lane;
+            for (int e = 0; e < EPL; ++e) z[jj][e] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) z[e] += al[w] * src[e];
-        }
+            for (int w = 0; w < kWaves; ++w) {
+                const float* src = g_big.accs + w * (kMaxRows * D) + row * D + EPL * lane;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) z[e] *= inv_nu;
-        // inverse rotation: unnormalised Hadamard over the D values (in-lane stage
-        // first, then lane distance 1 .. 32), divided by D below
-        if (EPL == 2) {
-            const float u0 = z[0], u1 = z[EPL - 1];
-            z[0] = u0 + u1;
-            z[EPL - 1] = u0 - u1;
+                for (int e = 0; e < EPL; ++e) z[jj][e] += al[w] * src[e];
+            }
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) z[jj][e] *= inv_nu;
+            // inverse rotation: unnormalised Hadamard over the D values (in-lane stage
+            // first, then lane distance 1 .. 32), divided by D below
+            if (EPL == 2) {
+                const float u0 = z[jj][0], u1 = z[jj][EPL - 1];
+                z[jj][0] = u0 + u1;
+                z[jj][EPL - 1] = u0 - u1;
+            }
         }
         auto stage = [&](auto off_tag) {
             constexpr int OFF = decltype(off_tag)::value;
             const float sg = (lane & OFF) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) z[e] = fmaf(sg, z[e], lane_xor<OFF>(z[e]));
+            for (int jj = 0; jj < RB; ++jj)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) z[jj][e] = fmaf(sg, z[jj][e], lane_xor<OFF>(z[jj][e]));
         };
         stage(std::integral_constant<int, 1>{});
         stage(std::integral_constant<int, 2>{});
@@ -734,29 +773,35 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         stage(std::integral_constant<int, 8>{});
         stage(std::integral_constant<int, 16>{});
         stage(std::integral_constant<int, 32>{});
-        const int k = P.agent0 + row / a.G;
-        const int head = g * a.G + row % a.G;
-        float o[EPL];
-        float denom;
-        if (a.has_sfx) {
-            const float mu = su_m[j];
-            const float M2 = fmaxf(M, mu);
-            const float ap = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
-            const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
-            denom = ap * L + au * su_l[j];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = ap * z[e] * (1.0f / D) + au * su_v[j][e];
-        } else {
-            denom = L;
+        for (int jj = 0; jj < RB; ++jj) {
+            const int j = j0 + jj;
+            const int row = wave + kWaves * j;
+            if (row >= R) break;
+            const int k = P.agent0 + row / a.G;
+            const int head = g * a.G + row % a.G;
+            float o[EPL];
+            float denom;
+            if (a.has_sfx) {
+                const float mu = su_m[j];
+                const float M2 = fmaxf(M[jj], mu);
+                const float ap = (M[jj] == -INFINITY) ? 0.0f : exp2f(M[jj] - M2);
+                const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
+                denom = ap * L[jj] + au * su_l[j];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = z[e] * (1.0f / D);
-        }
-        const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
-        float* out = a.out + (((uint64_t)a.agent_id[k] * a.lc + lj) * a.hq + head) * D + EPL * lane;
-        if constexpr (EPL == 2) {
-            *reinterpret_cast<float2*>(out) = make_float2(o[0] * rinv, o[1] * rinv);
-        } else {
-            out[0] = o[0] * rinv;
+                for (int e = 0; e < EPL; ++e) o[e] = ap * z[jj][e] * (1.0f / D) + au * su_v[j][e];
+            } else {
+                denom = L[jj];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[e] = z[jj][e] * (1.0f / D);
+            }
+            const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
+            float* out = a.out + (((uint64_t)out_agent[j] * a.lc + lj) * a.hq + head) * D + EPL * lane;
+            if constexpr (EPL == 2) {
+                *reinterpret_cast<float2*>(out) = make_float2(o[0] * rinv, o[1] * rinv);
+            } else {
+                out[0] = o[0] * rinv;
+            }
         }
     }
 }

@@ -168,6 +168,12 @@ def test_decode_workspace_query_and_errors():
     with pytest.raises(pk.PolyKVError):  # unequal token counts across the call's layers
         pk.agent_decode_attention([pool] * A, q, out)
     pool.n_tokens[1] = 70
+    for bad in ((_FakeT((A, lc, hq, d), (1 << 24) + 8), out), (q, _FakeT((A, lc, hq, d), (1 << 25) + 4, "f32"))):
+        with pytest.raises(pk.PolyKVError):  # q and out must be 16-byte aligned
+            pk.agent_decode_attention([pool] * A, *bad)
+    with pytest.raises(pk.PolyKVError):  # suffix arrays too
+        pk.agent_decode_attention([pool] * A, q, out, sfx_k=_FakeT((A, lc, 2, 16, d), (1 << 26) + 2), sfx_v=sk,
+                                  sfx_len=[0, 5, 16])
     # size is independent of pointers and grows with distinct pools
     p2 = _fake_pool(L=2, H=2, d=64, cap=100)
     p2.n_tokens[0] = p2.n_tokens[1] = 70

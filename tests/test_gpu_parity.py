@@ -183,6 +183,23 @@ def test_decode_is_deterministic_and_batch_independent(kernel):
     assert np.max(np.abs(solo[0] - a[1])) <= 1e-6 * max(1.0, np.max(np.abs(a[1])))
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_interleaved_pools(kernel):
+    # agents of two pools interleaved in the call: the launch regroups them by pool
+    print(f"[decode] interleaved pools kernel={kernel}", flush=True)
+    h = H()
+    w = wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=8, pool_tokens=150, sfx_tokens=8, n_pools=2)
+    pairs = [h.build_pair(w, p, layers=2) for p in range(2)]
+    pool_of = [0, 1, 0, 1, 1, 0]
+    A = len(pool_of)
+    q, q32 = h.make_queries(w, 3, range(A))
+    kd, vd, ksf, vsf = h.make_suffix(w, range(A), 2)
+    lens = [8, 0, 3, 8, 1, 5]
+    out = h.run_decode([pairs[p][0].pool for p in pool_of], q, (kd, vd), lens, kernel=kernel)
+    ref = h.oracle_decode(q32, pool_of, [p[1] for p in pairs], ksf, vsf, lens, w.n_kv_heads)
+    assert attention.max_rel_error(out, ref) <= TOL
+
+
 def _ramp_pool(h, slope, T=300, Hkv=2, d=128, seed=5):
     """A pool whose keys grow (slope > 0) or shrink along the tokens in one direction u."""
     rng = np.random.default_rng(seed)
