@@ -83,16 +83,14 @@ union H8 {
 // accumulator tile [64 rows][D], combined in a fixed order.
 constexpr int kMaxRows = 64;
 struct LoopLds {
+    uint32_t lut[256 * kLutCopies];  // first, so its address has zero low 15 bits
     uint8_t ring[kWaves][kStages][kStageBytes];
-    uint32_t lut[256 * kLutCopies];
 };
 union BigLds {
     LoopLds loop;
     float accs[kWaves * kMaxRows * 128];
 };
-__shared__ __align__(16) BigLds g_big;
-// fp16 query B operands of every lane: [RT][KS][64 lanes] x 16 bytes.
-__shared__ __align__(16) uint4 g_qop[4 * 4 * 64];
+__shared__ __align__(32768) BigLds g_big;
 __shared__ float g_m[kWaves][64];
 __shared__ float g_l[kWaves][64];
 __shared__ int g_flag;
@@ -136,53 +134,62 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
     return r;
 }
 
+// fp16 hi + lo parts of w0 = p0 * n0 and w1 = p1 * n1, packed (element 0 in the low
+// halves): hi = fp16(p * n) and lo = fp16(p * n - hi), each one fused multiply-add
+// with a single rounding (v_fma_mix with fp32 sources; the lo step reads hi as fp16)
+__device__ __forceinline__ void weights_hilo(float p0, float n0, float p1, float n1, uint32_t& hi, uint32_t& lo) {
+    asm("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+        "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+        "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "=&v"(hi), "=&v"(lo)
+        : "v"(p0), "v"(n0), "v"(p1), "v"(n1));
+}
+
 template <int NBYTES>
 struct Chunk {
     uint32_t w[NBYTES / 4];
 };
 
-// v_bfe_u32 kept opaque: the compiler would otherwise fold the later scaling of the
-// field into its shift and need a separate mask
-template <int OFF, int W>
-__device__ __forceinline__ uint32_t bfe(uint32_t w) {
-    uint32_t r;
-    asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "i"(OFF), "i"(W));
-    return r;
-}
-
-// 2b-bit field at bit position P of the chunk (P, b compile-time).
+// LDS byte offset of LUT entry `field` (a W-bit field at bit P of the chunk, P and W
+// compile-time) in this lane's copy: field * kLutCopies * 4 + lane_base.  The field
+// is shifted straight into place and masked; with the LUT 32 KB-aligned, the sum
+// with lane_base (< 128 above the LUT) has disjoint bits.
 template <int NBYTES, int P, int W>
-__device__ __forceinline__ uint32_t field(const Chunk<NBYTES>& c) {
+__device__ __forceinline__ uint32_t lut_offset(const Chunk<NBYTES>& c, uint32_t lane_base) {
     constexpr int wi = P >> 5, sh = P & 31;
+    constexpr uint32_t mask = ((1u << W) - 1u) << 7;  // kLutCopies * 4 = 128 bytes per entry
+    uint32_t x;
     if constexpr (sh + W <= 32) {
-        return bfe<sh, W>(c.w[wi]);
+        if constexpr (sh >= 7) x = (c.w[wi] >> (sh - 7)) & mask;
+        else x = (c.w[wi] << (7 - sh)) & mask;
     } else {
-        return bfe<0, W>(__builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh));
+        x = (__builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh) << 7) & mask;
     }
+    return x + lane_base;
 }
 
-// lutl = this lane's copy of the LUT (lut + lane % kLutCopies): entry e at lutl[e * kLutCopies]
 template <int NBYTES, int BITS, int NBI, int PI>
-__device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, const uint32_t* lutl) {
-    const uint32_t idx = field<NBYTES, 8 * BITS * NBI + 2 * BITS * PI, 2 * BITS>(c);
-    return lutl[idx * kLutCopies];
+__device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, uint32_t lane_base) {
+    const uint32_t off = lut_offset<NBYTES, 8 * BITS * NBI + 2 * BITS * PI, 2 * BITS>(c, lane_base);
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(off));
 }
 
 template <int NBYTES, int BITS, int NBI>
-__device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, const uint32_t* lutl) {
+__device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, uint32_t lane_base) {
     H8 r;
-    r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lutl);
-    r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lutl);
-    r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lutl);
-    r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lutl);
+    r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lane_base);
+    r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lane_base);
+    r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lane_base);
+    r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lane_base);
     return r.h;
 }
 
 template <int CB, int BITS, int NBI = 0>
-__device__ __forceinline__ void decode_all(half8 (&vb)[CB / BITS], const Chunk<CB>& c, const uint32_t* lutl) {
+__device__ __forceinline__ void decode_all(half8 (&vb)[CB / BITS], const Chunk<CB>& c, uint32_t lane_base) {
     if constexpr (NBI < CB / BITS) {
-        vb[NBI] = decode_b<CB, BITS, NBI>(c, lutl);
-        decode_all<CB, BITS, NBI + 1>(vb, c, lutl);
+        vb[NBI] = decode_b<CB, BITS, NBI>(c, lane_base);
+        decode_all<CB, BITS, NBI + 1>(vb, c, lane_base);
     }
 }
 
@@ -195,63 +202,108 @@ __device__ __forceinline__ void dma(const void* gsrc, void* ldst) {
     else __builtin_amdgcn_global_load_lds(gsrc, l, 4, 0, 0);
 }
 
-// All ring reads of one step in a single asm statement that ends with
-// s_waitcnt lgkmcnt(0), so no value can be used before it has arrived.
-// ka: this lane's K pieces (kr[i] at ka + i * 1024); va: its V code pieces (at
-// va + i * VSTRIDE); na: the norms of its 8 tokens (ns[0..1]) and their scales
-// (ns[2..3], 128 bytes on).
+// Raw ring contents of one step for this lane: K pieces (kr[i] at ka + i * 1024), V code
+// pieces (v[i] at va + i * VSTRIDE) and the norms (ns[0..1]) and scales (ns[2..3], 128
+// bytes on) of its 8 tokens.  ring_read issues the LDS reads without waiting;
+// ring_fence waits for them and passes every register through an asm output, so no
+// instruction can read them before the data has arrived.
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int CB> struct VPiece;
+template <> struct VPiece<8> { typedef uint32_t type; static constexpr int n = 2; };
+template <> struct VPiece<12> { typedef u32x3 type; static constexpr int n = 1; };
+template <> struct VPiece<16> { typedef u32x4 type; static constexpr int n = 1; };
+template <> struct VPiece<24> { typedef u32x3 type; static constexpr int n = 2; };
+template <> struct VPiece<32> { typedef u32x4 type; static constexpr int n = 2; };
+
 template <int NK, int CB>
-__device__ __forceinline__ void read_step(uint32_t ka, uint32_t va, uint32_t na, uint4 (&kr)[NK],
-                                          uint32_t (&cw)[CB / 4], uint4 (&ns)[4]) {
-    if constexpr (NK == 2 && CB == 8) {
-        
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b32 %2, %[va] offset:0\n\tds_read_b32 %3, %[va] offset:256\n\tds_read_b128 %4, %[na] offset:0\n\tds_read_b128 %5, %[na] offset:16\n\tds_read_b128 %6, %[na] offset:128\n\tds_read_b128 %7, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        
+struct RingRaw {
+    u32x4 kr[NK];
+    typename VPiece<CB>::type v[VPiece<CB>::n];
+    u32x4 ns[4];
+    // the CB code bytes as dwords
+    __device__ __forceinline__ void code_words(uint32_t (&cw)[CB / 4]) const {
+        constexpr int per = CB / 4 / VPiece<CB>::n;
+#pragma unroll
+        for (int i = 0; i < VPiece<CB>::n; ++i) {
+            if constexpr (per == 1) cw[i] = v[i];
+            else {
+#pragma unroll
+                for (int j = 0; j < per; ++j) cw[i * per + j] = v[i][j];
+            }
+        }
     }
-    if constexpr (NK == 2 && CB == 12) {
-        u32x3 v0;
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b96 %2, %[va]\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        cw[0] = v0[0]; cw[1] = v0[1]; cw[2] = v0[2];
-    }
-    if constexpr (NK == 2 && CB == 16) {
-        uint4 v0;
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[va]\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w;
-    }
-    if constexpr (NK == 4 && CB == 16) {
-        uint4 v0;
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va]\n\tds_read_b128 %5, %[na] offset:0\n\tds_read_b128 %6, %[na] offset:16\n\tds_read_b128 %7, %[na] offset:128\n\tds_read_b128 %8, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w;
-    }
-    if constexpr (NK == 4 && CB == 24) {
-        u32x3 v0, v1;
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b96 %4, %[va] offset:0\n\tds_read_b96 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(v1), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        cw[0] = v0[0]; cw[1] = v0[1]; cw[2] = v0[2]; cw[3] = v1[0]; cw[4] = v1[1]; cw[5] = v1[2];
-    }
-    if constexpr (NK == 4 && CB == 32) {
-        uint4 v0, v1;
-        asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va] offset:0\n\tds_read_b128 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(v0), "=&v"(v1), "=&v"(ns[0]), "=&v"(ns[1]), "=&v"(ns[2]), "=&v"(ns[3])
-                     : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
-                     : "memory");
-        cw[0] = v0.x; cw[1] = v0.y; cw[2] = v0.z; cw[3] = v0.w; cw[4] = v1.x; cw[5] = v1.y; cw[6] = v1.z; cw[7] = v1.w;
-    }
+};
+
+template <int NK, int CB>
+__device__ __forceinline__ void ring_read(uint32_t ka, uint32_t va, uint32_t na, RingRaw<NK, CB>& r);
+template <int NK, int CB>
+__device__ __forceinline__ void ring_fence(RingRaw<NK, CB>& r);
+template <>
+__device__ __forceinline__ void ring_read<2, 8>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<2, 8>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b32 %2, %[va] offset:0\n\tds_read_b32 %3, %[va] offset:256\n\tds_read_b128 %4, %[na] offset:0\n\tds_read_b128 %5, %[na] offset:16\n\tds_read_b128 %6, %[na] offset:128\n\tds_read_b128 %7, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<2, 8>(RingRaw<2, 8>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
+}
+template <>
+__device__ __forceinline__ void ring_read<2, 12>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<2, 12>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b96 %2, %[va] offset:0\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.v[0]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<2, 12>(RingRaw<2, 12>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.v[0]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
+}
+template <>
+__device__ __forceinline__ void ring_read<2, 16>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<2, 16>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[va] offset:0\n\tds_read_b128 %3, %[na] offset:0\n\tds_read_b128 %4, %[na] offset:16\n\tds_read_b128 %5, %[na] offset:128\n\tds_read_b128 %6, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.v[0]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<2, 16>(RingRaw<2, 16>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.v[0]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
+}
+template <>
+__device__ __forceinline__ void ring_read<4, 16>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<4, 16>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va] offset:0\n\tds_read_b128 %5, %[na] offset:0\n\tds_read_b128 %6, %[na] offset:16\n\tds_read_b128 %7, %[na] offset:128\n\tds_read_b128 %8, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.kr[2]), "=&v"(r.kr[3]), "=&v"(r.v[0]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<4, 16>(RingRaw<4, 16>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.kr[2]), "+v"(r.kr[3]), "+v"(r.v[0]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
+}
+template <>
+__device__ __forceinline__ void ring_read<4, 24>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<4, 24>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b96 %4, %[va] offset:0\n\tds_read_b96 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.kr[2]), "=&v"(r.kr[3]), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<4, 24>(RingRaw<4, 24>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.kr[2]), "+v"(r.kr[3]), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
+}
+template <>
+__device__ __forceinline__ void ring_read<4, 32>(uint32_t ka, uint32_t va, uint32_t na, RingRaw<4, 32>& r) {
+    asm volatile("ds_read_b128 %0, %[ka] offset:0\n\tds_read_b128 %1, %[ka] offset:1024\n\tds_read_b128 %2, %[ka] offset:2048\n\tds_read_b128 %3, %[ka] offset:3072\n\tds_read_b128 %4, %[va] offset:0\n\tds_read_b128 %5, %[va] offset:1024\n\tds_read_b128 %6, %[na] offset:0\n\tds_read_b128 %7, %[na] offset:16\n\tds_read_b128 %8, %[na] offset:128\n\tds_read_b128 %9, %[na] offset:144"
+                 : "=&v"(r.kr[0]), "=&v"(r.kr[1]), "=&v"(r.kr[2]), "=&v"(r.kr[3]), "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.ns[0]), "=&v"(r.ns[1]), "=&v"(r.ns[2]), "=&v"(r.ns[3])
+                 : [ka] "v"(ka), [va] "v"(va), [na] "v"(na)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void ring_fence<4, 32>(RingRaw<4, 32>& r) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r.kr[0]), "+v"(r.kr[1]), "+v"(r.kr[2]), "+v"(r.kr[3]), "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.ns[0]), "+v"(r.ns[1]), "+v"(r.ns[2]), "+v"(r.ns[3]) :: "memory");
 }
 
 template <int D, int BITS>
@@ -378,7 +430,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i);
     // bf16 values convert exactly (8 significant bits) within fp16's range, fp32
     // values are split into fp16 hi + lo operands
-    half8 qreg[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
+    half8 qreg[RT][KS];  // kept in registers for the whole unit
     half8 qlo[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
     float qoff[RT];
 #pragma unroll
@@ -414,12 +466,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                     sum += (float)ll[0] + (float)ll[1];
                 }
             }
-            if constexpr (QSPLIT) {
-                qreg[rt][k] = hv.h;
-                qlo[rt][k] = lv.h;
-            } else if (wave == 0) {
-                g_qop[(rt * KS + k) * 64 + lane] = hv.v;
-            }
+            qreg[rt][k] = hv.h;
+            if constexpr (QSPLIT) qlo[rt][k] = lv.h;
         }
         // -1152 * sum of the row's fp16 query values: cancels the offset carried by K
         sum += __shfl_xor(sum, 16, 64);
@@ -439,30 +487,30 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
     __syncthreads();  // LUT and query operands ready
 
-    const uint32_t* lutl = g_big.loop.lut + (lane & (kLutCopies - 1));
+    const uint32_t lut_lane = lds_addr(g_big.loop.lut) + 4u * (lane & (kLutCopies - 1));  // this lane's LUT copy
     const uint32_t ring_a = lds_addr(ring);
     const float fs = a.sm_log2;
 
-    // wait until the loads of this wavefront's step `it` have landed (steps are
-    // issued in order, kStages - 1 ahead of use)
-    auto wait_step = [&](int it) {
-        const int ahead = min(my_steps - 1 - it, kStages - 2);  // steps issued after it
-        if (ahead >= 2) wait_vmcnt<2 * SL::NDMA>();
-        else if (ahead == 1) wait_vmcnt<SL::NDMA>();
+    // wait until at most `groups` steps' loads issued after the one needed are in
+    // flight (each step is SL::NDMA load instructions, completed in order)
+    auto wait_groups = [&](int groups) {
+        if (groups >= 2) wait_vmcnt<2 * SL::NDMA>();
+        else if (groups == 1) wait_vmcnt<SL::NDMA>();
         else wait_vmcnt<0>();
     };
-    // the ring slot of step `it`: K as fp16 operands (1152 + k, exact; the offset is
-    // removed by the accumulator init), V code chunk, norms and scales
-    auto read_slot = [&](int it, half8 (&ka)[2][KS], Chunk<CB>& ch, uint4 (&ns)[4]) {
+    // ring slot of step `it` -> registers (no wait: see ring_fence)
+    using Raw = RingRaw<SL::NK, CB>;
+    auto ring_issue = [&](int it, Raw& r) {
         const uint32_t sa = ring_a + (it % kStages) * kStageBytes;
-        uint4 kr[SL::NK];
-        read_step<SL::NK, CB>(sa + SL::KOFF + lane * 16, sa + SL::VOFF + lane * SL::VLANE, sa + SL::NOFF + 32 * lg,
-                              kr, ch.w, ns);
+        ring_read<SL::NK, CB>(sa + SL::KOFF + lane * 16, sa + SL::VOFF + lane * SL::VLANE, sa + SL::NOFF + 32 * lg, r);
+    };
+    // K as fp16 operands (1152 + k, exact; the offset is removed by the accumulator init)
+    auto convert_k = [&](const Raw& r, half8 (&ka)[2][KS]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                const uint4 v = kr[u * (DL / 16) + k / 2];
+                const u32x4 v = r.kr[u * (DL / 16) + k / 2];
                 H8 h;
                 i8x4_to_h4_offset((k & 1) ? v.z : v.x, h.u[0], h.u[1]);
                 i8x4_to_h4_offset((k & 1) ? v.w : v.y, h.u[2], h.u[3]);
@@ -473,23 +521,18 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // 8 lg + 4 u + j of row 16 rt + rl in S[u][j] (q . k for the int8 codes k)
     auto scores = [&](const half8 (&ka)[2][KS], int rt, f32x4 (&S)[2]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x4 sacc = {qoff[rt], qoff[rt], qoff[rt], qoff[rt]};
+        for (int u = 0; u < 2; ++u) S[u] = f32x4{qoff[rt], qoff[rt], qoff[rt], qoff[rt]};
+        // the two tiles' chains interleaved
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                if constexpr (QSPLIT) {
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qreg[rt][k], sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qlo[rt][k], sacc, 0, 0, 0);
-                } else {
-                    H8 q;
-                    q.v = g_qop[(rt * KS + k) * 64 + lane];
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], q.h, sacc, 0, 0, 0);
-                }
+        for (int k = 0; k < KS; ++k) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qreg[rt][k], S[u], 0, 0, 0);
+                if constexpr (QSPLIT) S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qlo[rt][k], S[u], 0, 0, 0);
             }
-            S[u] = sacc;
         }
     };
-    auto norms = [&](const uint4 (&ns)[4], float (&nn)[8], float (&ff)[8]) {
+    auto norms = [&](const u32x4 (&ns)[4], float (&nn)[8], float (&ff)[8]) {
         const uint32_t w[16] = {ns[0].x, ns[0].y, ns[0].z, ns[0].w, ns[1].x, ns[1].y, ns[1].z, ns[1].w,
                                 ns[2].x, ns[2].y, ns[2].z, ns[2].w, ns[3].x, ns[3].y, ns[3].z, ns[3].w};
 #pragma unroll
@@ -510,13 +553,14 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) cref[rt] = 0.0f;
     if (my_steps > 0) {
-        wait_step(0);
+        wait_groups(min(my_steps, kStages - 1) - 1);  // steps 0 .. kStages - 2 were issued
+        Raw r;
+        ring_issue(0, r);
+        ring_fence(r);
         half8 ka[2][KS];
-        Chunk<CB> ch;
-        uint4 ns[4];
-        read_slot(0, ka, ch, ns);
+        convert_k(r, ka);
         float nn[8], ff[8];
-        norms(ns, nn, ff);
+        norms(r.ns, nn, ff);
         const int t0 = tb + wave * kStep;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -546,31 +590,36 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             for (int it = 0; it < kStages - 1; ++it)
                 if (it < my_steps) issue(it);
         }
-        // one 32-token step; TAIL masks tokens at or past the end of the split
-        auto step = [&](const int it, auto tail_tag) {
+        // One 32-token step.  The ring reads of the next step are issued once this
+        // step's last LDS reads (the LUT) have completed, and land while the softmax and
+        // the P.V products run: nothing else reads LDS in between.  TAIL masks tokens at
+        // or past the end of the split.
+        auto step = [&](const int it, Raw& cur, Raw& nxt, auto tail_tag, const bool prefetch) {
             constexpr bool TAIL = decltype(tail_tag)::value;
             const int t0 = tb + (wave + it * kWaves) * kStep;
-            if (it + kStages - 1 < my_steps) {
-                issue(it + kStages - 1);
-                wait_vmcnt<(kStages - 1) * SL::NDMA>();
-            } else {
-                wait_step(it);
+            if (prefetch) {
+                if (it + kStages - 1 < my_steps) issue(it + kStages - 1);  // slot of step it - 1, already read
+                wait_groups(min(kStages - 2, my_steps - 2 - it));       // loads of step it + 1 landed
             }
-            half8 ka[2][KS];
             Chunk<CB> ch;
-            uint4 ns[4];
-            read_slot(it, ka, ch, ns);
+            cur.code_words(ch.w);
             // V centroids for the 8 tokens x NB dims of this lane, from the LUT
             half8 vb[NB];
-            decode_all<CB, BITS>(vb, ch, lutl);
+            decode_all<CB, BITS>(vb, ch, lut_lane);
+            half8 ka[2][KS];
+            convert_k(cur, ka);
             float nn[8], ff[8];
-            norms(ns, nn, ff);
+            norms(cur.ns, nn, ff);
             bool ok[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 ok[i] = !TAIL || (t0 + 8 * lg + i < te);
                 if (TAIL) nn[i] = ok[i] ? nn[i] : 0.0f;
             }
+            // LUT values in registers; the compiler's own LDS reads of this step end here
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch) ring_issue(it + 1, nxt);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 f32x4 S[2];
@@ -589,11 +638,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                     const float p0 = __builtin_amdgcn_exp2f(x[i]);
                     const float p1 = __builtin_amdgcn_exp2f(x[i + 1]);
                     lsum[rt] += p0 + p1;
-                    const half2v hi = {(_Float16)(p0 * nn[i]), (_Float16)(p1 * nn[i + 1])};
-                    const half2v lo = {(_Float16)fmaf(p0, nn[i], -(float)hi[0]),
-                                       (_Float16)fmaf(p1, nn[i + 1], -(float)hi[1])};
-                    wh.u[i / 2] = __builtin_bit_cast(uint32_t, hi);
-                    wl.u[i / 2] = __builtin_bit_cast(uint32_t, lo);
+                    weights_hilo(p0, nn[i], p1, nn[i + 1], wh.u[i / 2], wl.u[i / 2]);
                 }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -601,13 +646,21 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                     acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl.h, vb[nb], acc[rt][nb], 0, 0, 0);
                 }
             }
+            if (prefetch) ring_fence(nxt);
         };
-        // only the step holding the end of the split can be partial: it is the last
-        // step of one wavefront, run after the loop so the loop body has no masking
         const bool has_tail = my_steps > 0 && (te - tb) % kStep != 0 && wave == (nsteps - 1) % kWaves;
         const int full = my_steps - (has_tail ? 1 : 0);
-        for (int it = 0; it < full; ++it) step(it, std::false_type{});
-        if (has_tail) step(full, std::true_type{});
+        Raw cur, nxt;
+        if (my_steps > 0) {
+            wait_groups(min(my_steps - 1, kStages - 2));
+            ring_issue(0, cur);
+            ring_fence(cur);
+        }
+        for (int it = 0; it < full; ++it) {
+            step(it, cur, nxt, std::false_type{}, it + 1 < my_steps);
+            cur = nxt;
+        }
+        if (has_tail) step(full, cur, nxt, std::true_type{}, false);
         // any row over the limit? then every wave re-runs with the exact row maxima
         if (tid == 0) g_flag = 0;
         __syncthreads();
