@@ -193,13 +193,16 @@ __device__ __forceinline__ void decode_all(half8 (&vb)[CB / BITS], const Chunk<C
     }
 }
 
-// Direct-to-LDS load: every lane's `SIZE` bytes at gsrc land at ldst + lane * SIZE.
+// Direct-to-LDS load: every lane's `SIZE` bytes at base + off land at ldst + lane * SIZE
+// (base wave-uniform, off per lane: the scalar-base form of the instruction).
+typedef const __attribute__((address_space(1))) uint8_t* gptr_t;
 template <int SIZE>
-__device__ __forceinline__ void dma(const void* gsrc, void* ldst) {
+__device__ __forceinline__ void dma(const void* base, uint32_t off, void* ldst) {
     auto* l = reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(ldst));
-    if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(gsrc, l, 16, 0, 0);
-    else if constexpr (SIZE == 12) __builtin_amdgcn_global_load_lds(gsrc, l, 12, 0, 0);
-    else __builtin_amdgcn_global_load_lds(gsrc, l, 4, 0, 0);
+    gptr_t g = reinterpret_cast<gptr_t>(reinterpret_cast<uintptr_t>(base)) + off;
+    if constexpr (SIZE == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+    else if constexpr (SIZE == 12) __builtin_amdgcn_global_load_lds(g, l, 12, 0, 0);
+    else __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
 }
 
 // Raw ring contents of one step for this lane: K pieces (kr[i] at ka + i * 1024), V code
@@ -367,32 +370,41 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     const int ktok0 = 8 * (rl >> 2) + (rl & 3);
     uint8_t* ring = &g_big.loop.ring[wave][0][0];
 
+    // Per-lane byte offsets of a step's pieces, fixed across steps: each load below is a
+    // wave-uniform base (scalar) plus this 32-bit offset.
+    uint32_t koff[SL::NK];
+#pragma unroll
+    for (int i = 0; i < SL::NK; ++i) {
+        const int u = i / (DL / 16), h = i % (DL / 16);
+        koff[i] = (uint32_t)((ktok0 + 4 * u) * D + lg * DL + 16 * h);
+    }
+    const uint32_t voff = (uint32_t)(CB * lane);  // this lane's code chunk in the step's 4 groups
+    // norms (lanes 0-31) and K scales (lanes 32-63) of the step's 32 tokens
+    const bool nlane = lane < 32;
+    const uint32_t noff = 4u * (uint32_t)(lane & 31);
     auto issue = [&](int it) {  // DMA of this wavefront's it-th step into ring slot it % kStages
         const int t0 = tb + (wave + it * kWaves) * kStep;
         uint8_t* st = ring + (it % kStages) * kStageBytes;
+        const int8_t* kstep = kq + (uint64_t)t0 * D;
 #pragma unroll
-        for (int i = 0; i < SL::NK; ++i) {
-            const int u = i / (DL / 16), h = i % (DL / 16);
-            dma<16>(kq + (uint64_t)(t0 + ktok0 + 4 * u) * D + lg * DL + 16 * h, st + SL::KOFF + i * 1024);
-        }
-        // this lane's code chunk: bytes [CB * lane, CB * lane + CB) of the step's 4 groups
-        const uint8_t* vsrc = vc + (uint64_t)(t0 / kGroupTokens) * (D * BITS) + CB * lane;
+        for (int i = 0; i < SL::NK; ++i) dma<16>(kstep, koff[i], st + SL::KOFF + i * 1024);
+        const uint8_t* vsrc = vc + (uint64_t)(t0 / kGroupTokens) * (D * BITS);
         if constexpr (CB == 8) {
-            dma<4>(vsrc, st + SL::VOFF);
-            dma<4>(vsrc + 4, st + SL::VOFF + SL::VSTRIDE);
+            dma<4>(vsrc, voff, st + SL::VOFF);
+            dma<4>(vsrc, voff + 4, st + SL::VOFF + SL::VSTRIDE);
         } else if constexpr (CB == 12) {
-            dma<12>(vsrc, st + SL::VOFF);
+            dma<12>(vsrc, voff, st + SL::VOFF);
         } else if constexpr (CB == 16) {
-            dma<16>(vsrc, st + SL::VOFF);
+            dma<16>(vsrc, voff, st + SL::VOFF);
         } else if constexpr (CB == 24) {
-            dma<12>(vsrc, st + SL::VOFF);
-            dma<12>(vsrc + 12, st + SL::VOFF + SL::VSTRIDE);
+            dma<12>(vsrc, voff, st + SL::VOFF);
+            dma<12>(vsrc, voff + 12, st + SL::VOFF + SL::VSTRIDE);
         } else {
-            dma<16>(vsrc, st + SL::VOFF);
-            dma<16>(vsrc + 16, st + SL::VOFF + SL::VSTRIDE);
+            dma<16>(vsrc, voff, st + SL::VOFF);
+            dma<16>(vsrc, voff + 16, st + SL::VOFF + SL::VSTRIDE);
         }
-        const float* nsrc = lane < 32 ? vn + t0 + lane : ks + t0 + (lane - 32);
-        dma<4>(nsrc, st + SL::NOFF);
+        // one load: lanes 0-31 read norms, 32-63 scales (per-lane base select, no 64-bit math)
+        dma<4>(nlane ? (const void*)(vn + t0) : (const void*)(ks + t0), noff, st + SL::NOFF);
     };
 
     // ---- set-up loads first, all at once: this lane's query chunks (8 values per
@@ -594,7 +606,12 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         // step's last LDS reads (the LUT) have completed, and land while the softmax and
         // the P.V products run: nothing else reads LDS in between.  TAIL masks tokens at
         // or past the end of the split.
-        auto step = [&](const int it, Raw& cur, Raw& nxt, auto tail_tag, const bool prefetch) {
+        // One 32-token step from the registers of `raw`, which then receive the next
+        // step's ring contents: those reads are issued once this step's own LDS reads
+        // (the LUT) have completed, and land while the softmax and the P.V products run
+        // (nothing else reads LDS in between).  TAIL masks tokens at or past the end of
+        // the split.
+        auto step = [&](const int it, Raw& raw, auto tail_tag, const bool prefetch) {
             constexpr bool TAIL = decltype(tail_tag)::value;
             const int t0 = tb + (wave + it * kWaves) * kStep;
             if (prefetch) {
@@ -602,34 +619,36 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 wait_groups(min(kStages - 2, my_steps - 2 - it));       // loads of step it + 1 landed
             }
             Chunk<CB> ch;
-            cur.code_words(ch.w);
+            raw.code_words(ch.w);
             // V centroids for the 8 tokens x NB dims of this lane, from the LUT
             half8 vb[NB];
             decode_all<CB, BITS>(vb, ch, lut_lane);
             half8 ka[2][KS];
-            convert_k(cur, ka);
+            convert_k(raw, ka);
             float nn[8], ff[8];
-            norms(cur.ns, nn, ff);
+            norms(raw.ns, nn, ff);
             bool ok[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 ok[i] = !TAIL || (t0 + 8 * lg + i < te);
                 if (TAIL) nn[i] = ok[i] ? nn[i] : 0.0f;
             }
-            // LUT values in registers; the compiler's own LDS reads of this step end here
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            // scores of the first row tile while the LUT reads complete
+            f32x4 S[2];
+            scores(ka, 0, S);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LUT values in registers
             __builtin_amdgcn_sched_barrier(0);
-            if (prefetch) ring_issue(it + 1, nxt);
+            if (prefetch) ring_issue(it + 1, raw);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                f32x4 S[2];
-                scores(ka, rt, S);
                 float x[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     x[i] = fmaf(S[i >> 2][i & 3], ff[i], cref[rt]);
                     if (TAIL) x[i] = ok[i] ? x[i] : -INFINITY;
                 }
+                // the next row tile's scores overlap this tile's softmax
+                if (rt + 1 < RT) scores(ka, rt + 1, S);
                 xmax[rt] = max3(max3(xmax[rt], x[0], x[1]), max3(x[2], x[3], x[4]), max3(x[5], x[6], x[7]));
                 // weights w = p' * vn as fp16 hi + lo (w - hi, rounded once more): ~2^-22 relative
                 H8 wh, wl;
@@ -646,21 +665,18 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                     acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl.h, vb[nb], acc[rt][nb], 0, 0, 0);
                 }
             }
-            if (prefetch) ring_fence(nxt);
+            if (prefetch) ring_fence(raw);
         };
         const bool has_tail = my_steps > 0 && (te - tb) % kStep != 0 && wave == (nsteps - 1) % kWaves;
         const int full = my_steps - (has_tail ? 1 : 0);
-        Raw cur, nxt;
+        Raw raw;
         if (my_steps > 0) {
             wait_groups(min(my_steps - 1, kStages - 2));
-            ring_issue(0, cur);
-            ring_fence(cur);
+            ring_issue(0, raw);
+            ring_fence(raw);
         }
-        for (int it = 0; it < full; ++it) {
-            step(it, cur, nxt, std::false_type{}, it + 1 < my_steps);
-            cur = nxt;
-        }
-        if (has_tail) step(full, cur, nxt, std::true_type{}, false);
+        for (int it = 0; it < full; ++it) step(it, raw, std::false_type{}, it + 1 < my_steps);
+        if (has_tail) step(full, raw, std::true_type{}, false);
         // any row over the limit? then every wave re-runs with the exact row maxima
         if (tid == 0) g_flag = 0;
         __syncthreads();
