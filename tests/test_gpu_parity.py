@@ -140,6 +140,31 @@ def test_decode_matches_oracle(case, kernel):
     assert err <= TOL, err
 
 
+# suffixes past one 256-token chunk of the suffix kernel, every group size it specialises
+LONG_SUFFIX_CASES = {
+    "g4_d128_chunk_edges": (wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=2, n_q_heads=8, pool_tokens=64,
+                                                 sfx_tokens=600), [600, 256, 257, 513, 1, 0]),
+    "g1_d128": (wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=2, n_q_heads=2, pool_tokens=40, sfx_tokens=300),
+                [300, 17, 256]),
+    "g2_d128": (wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=4, pool_tokens=40, sfx_tokens=290),
+                [290, 129]),
+    "g3_d64": (wl.SMOLLM2.replace(n_layers=1, n_kv_heads=2, n_q_heads=6, pool_tokens=50, sfx_tokens=300),
+               [300, 255, 0]),
+    "g6_d128": (wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=2, n_q_heads=12, pool_tokens=40, sfx_tokens=270),
+                [270, 31]),
+    "g8_d64": (wl.SMOLLM2.replace(n_layers=1, n_kv_heads=1, n_q_heads=8, pool_tokens=40, sfx_tokens=520),
+               [520, 512]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(LONG_SUFFIX_CASES))
+def test_decode_long_suffix(case):
+    w, lens = LONG_SUFFIX_CASES[case]
+    print(f"[decode] long suffix {case}", flush=True)
+    err, _ = _decode_case(w, w.n_layers, lens, pk.KERNEL_MFMA)
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("splits", [1, 3, 50])
 def test_decode_split_plans_agree(splits, kernel):
