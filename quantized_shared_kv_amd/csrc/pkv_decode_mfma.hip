@@ -193,6 +193,12 @@ __device__ __forceinline__ void decode_all(half8 (&vb)[CB / BITS], const Chunk<C
     }
 }
 
+// Workgroup barrier for LDS traffic only: global loads still in flight (the
+// suffix records fetched ahead of the combine, the ring's direct-to-LDS loads,
+// which every wave waits for on its own before reading its slots) are not
+// waited for, as a full __syncthreads() would.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Direct-to-LDS load: every lane's `SIZE` bytes at base + off land at ldst + lane * SIZE
 // (base wave-uniform, off per lane: the scalar-base form of the instruction).
 typedef const __attribute__((address_space(1))) uint8_t* gptr_t;
@@ -497,7 +503,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             g_big.loop.lut[i0 + tid] = pack_h2(c0, c1);
         }
     }
-    __syncthreads();  // LUT and query operands ready
+    lds_barrier();  // LUT and query operands ready
 
     const uint32_t lut_lane = lds_addr(g_big.loop.lut) + 4u * (lane & (kLutCopies - 1));  // this lane's LUT copy
     const uint32_t ring_a = lds_addr(ring);
@@ -679,7 +685,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         if (has_tail) step(full, raw, std::true_type{}, false);
         // any row over the limit? then every wave re-runs with the exact row maxima
         if (tid == 0) g_flag = 0;
-        __syncthreads();
+        lds_barrier();
         bool over = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -691,7 +697,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             if (lg == 0) g_m[wave][16 * rt + rl] = my_steps > 0 ? t - cref[rt] : -INFINITY;
         }
         if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) atomicOr(&g_flag, 1);
-        __syncthreads();
+        lds_barrier();
         if (g_flag == 0) break;
         // re-run reference: the exact row max over the workgroup (no score exceeds it)
 #pragma unroll
@@ -701,7 +707,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             for (int w = 0; w < kWaves; ++w) M = fmaxf(M, g_m[w][16 * rt + rl]);
             cref[rt] = (float)lnu - M;
         }
-        __syncthreads();
+        lds_barrier();
     }
     const float inv_nu = 1.0f / nu;
     float m[RT];
@@ -712,34 +718,36 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
 
     // ---- combine the 4 wavefronts (fixed order, so results do not depend on timing)
-    constexpr int EPL = D / 64;
     constexpr int RPW = kMaxRows / kWaves;  // rows finished per wavefront
+    constexpr int FD = D / 16;              // fused finish: dimensions per lane (16 lanes per row)
+    constexpr int FI = RPW / 4;             // fused finish: rows per lane (4 rows per wavefront pass)
     const bool fused = a.fused != 0;
-    // fused finish with a suffix: fetch this wavefront's suffix records now, so their
-    // latency overlaps the combine (row = wave + kWaves * j)
-    float su_m[RPW], su_l[RPW], su_v[RPW][EPL];
-    int out_agent[RPW];
+    // fused finish: lane (fq, fl) handles rows wave + kWaves * (4 i + fq), i < FI, dims
+    // FD fl .. FD fl + FD - 1.  Its rows' agents, heads and suffix records are fetched
+    // now, so their latency overlaps the combine
+    const int fq = lane >> 4, fl = lane & 15;
+    float su_m[FI], su_l[FI], su_v[FI][FD];
+    int f_row[FI], f_head[FI], f_agent[FI];
+    if (fused) {
+        const float rG = __builtin_amdgcn_rcpf((float)a.G);
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-        const int row = min(wave + kWaves * j, R - 1);
-        out_agent[j] = P.agent_base >= 0 ? P.agent_base + row / a.G : a.agent_id[P.agent0 + row / a.G];
-    }
-    if (fused && a.has_sfx) {
+        for (int i = 0; i < FI; ++i) {
+            const int row = min(wave + kWaves * (4 * i + fq), R - 1);  // rows past R: computed, not stored
+            const int ka = (int)(((float)row + 0.5f) * rG);  // row / G, exact for rows < 2^20
+            f_row[i] = row;
+            f_head[i] = g * a.G + row - ka * a.G;
+            f_agent[i] = P.agent_base >= 0 ? P.agent_base + ka : a.agent_id[P.agent0 + ka];
+            su_m[i] = -INFINITY;
+            su_l[i] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const int row = wave + kWaves * j;
-            su_m[j] = -INFINITY;
-            su_l[j] = 0.0f;
+            for (int e = 0; e < FD; ++e) su_v[i][e] = 0.0f;
+            if (a.has_sfx) {
+                const float* ru =
+                    a.part + a.sfx_part_off + (((uint64_t)(P.agent0 + ka) * a.lc + lj) * a.hq + f_head[i]) * (2 + D);
+                su_m[i] = ru[0];
+                su_l[i] = ru[1];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) su_v[j][e] = 0.0f;
-            if (row < R) {
-                const int k = P.agent0 + row / a.G;
-                const int head = g * a.G + row % a.G;
-                const float* ru = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + head) * (2 + D);
-                su_m[j] = ru[0];
-                su_l[j] = ru[1];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) su_v[j][e] = ru[2 + EPL * lane + e];
+                for (int e = 0; e < FD; ++e) su_v[i][e] = ru[2 + FD * fl + e];
             }
         }
     }
@@ -752,7 +760,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             g_l[wave][16 * rt + rl] = lsum[rt];
         }
     }
-    __syncthreads();  // every wave is done with the ring and the LUT
+    lds_barrier();  // every wave is done with the ring and the LUT
     // this wave's tile: row 16 rt + 4 lg + j, dims NB * rl .. NB * rl + NB - 1
     float* mine = g_big.accs + wave * (kMaxRows * D);
 #pragma unroll
@@ -765,7 +773,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 *reinterpret_cast<float4*>(dst + 4 * h) =
                     make_float4(acc[rt][4 * h][j], acc[rt][4 * h + 1][j], acc[rt][4 * h + 2][j], acc[rt][4 * h + 3][j]);
         }
-    __syncthreads();
+    lds_barrier();
     // row combine: M = max of the waves' references, weights 2^(m_w - M)
     auto row_weights = [&](int row, float (&al)[kWaves], float& M, float& L) {
         M = -INFINITY;
@@ -775,7 +783,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float mw = g_m[w][row];
-            al[w] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+            al[w] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
             L += al[w] * g_l[w][row];
         }
     };
@@ -798,79 +806,66 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
         return;
     }
-    // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store;
-    // four rows at a time so their lane exchanges overlap
-    constexpr int RB = 4;
+    // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store.
+    // The Hadamard butterflies run over the dimension bits: the low log2 FD in-lane, the
+    // high four across the row's 16 lanes (lane distance 1, 2, 4, 8: DPP moves only)
 #pragma unroll
-    for (int j0 = 0; j0 < RPW; j0 += RB) {
-        if (wave + kWaves * j0 >= R) break;
-        float z[RB][EPL], M[RB], L[RB];
+    for (int i = 0; i < FI; ++i) {
+        if (wave + kWaves * 4 * i >= R) break;  // no row of this pass is stored
+        const int row = f_row[i];
+        float al[kWaves], M, L;
+        row_weights(row, al, M, L);
+        float z[FD];
 #pragma unroll
-        for (int jj = 0; jj < RB; ++jj) {
-            const int row = min(wave + kWaves * (j0 + jj), R - 1);  // rows past R: computed, not stored
-            float al[kWaves];
-            row_weights(row, al, M[jj], L[jj]);
+        for (int e = 0; e < FD; ++e) z[e] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) z[jj][e] = 0.0f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float* src = g_big.accs + w * (kMaxRows * D) + row * D + FD * fl;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float* src = g_big.accs + w * (kMaxRows * D) + row * D + EPL * lane;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) z[jj][e] += al[w] * src[e];
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) z[jj][e] *= inv_nu;
-            // inverse rotation: unnormalised Hadamard over the D values (in-lane stage
-            // first, then lane distance 1 .. 32), divided by D below
-            if (EPL == 2) {
-                const float u0 = z[jj][0], u1 = z[jj][EPL - 1];
-                z[jj][0] = u0 + u1;
-                z[jj][EPL - 1] = u0 - u1;
+            for (int e4 = 0; e4 < FD; e4 += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(src + e4);
+                z[e4] = fmaf(al[w], v.x, z[e4]);
+                z[e4 + 1] = fmaf(al[w], v.y, z[e4 + 1]);
+                z[e4 + 2] = fmaf(al[w], v.z, z[e4 + 2]);
+                z[e4 + 3] = fmaf(al[w], v.w, z[e4 + 3]);
             }
         }
+#pragma unroll
+        for (int h = 1; h < FD; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < FD; ++e)
+                if (!(e & h)) {
+                    const float u0 = z[e], u1 = z[e + h];
+                    z[e] = u0 + u1;
+                    z[e + h] = u0 - u1;
+                }
         auto stage = [&](auto off_tag) {
             constexpr int OFF = decltype(off_tag)::value;
             const float sg = (lane & OFF) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int jj = 0; jj < RB; ++jj)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) z[jj][e] = fmaf(sg, z[jj][e], lane_xor<OFF>(z[jj][e]));
+            for (int e = 0; e < FD; ++e) z[e] = fmaf(sg, z[e], lane_xor_row<OFF>(z[e], lane));
         };
         stage(std::integral_constant<int, 1>{});
         stage(std::integral_constant<int, 2>{});
         stage(std::integral_constant<int, 4>{});
         stage(std::integral_constant<int, 8>{});
-        stage(std::integral_constant<int, 16>{});
-        stage(std::integral_constant<int, 32>{});
+        const float mu = su_m[i];
+        const float M2 = fmaxf(M, mu);
+        const float ap = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - M2);
+        const float au = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M2);
+        const float denom = ap * L + au * su_l[i];
+        const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
+        const float sp_ = ap * inv_nu * (1.0f / D) * rinv;
+        const float su_ = au * rinv;
+        float o[FD];
 #pragma unroll
-        for (int jj = 0; jj < RB; ++jj) {
-            const int j = j0 + jj;
-            const int row = wave + kWaves * j;
-            if (row >= R) break;
-            const int k = P.agent0 + row / a.G;
-            const int head = g * a.G + row % a.G;
-            float o[EPL];
-            float denom;
-            if (a.has_sfx) {
-                const float mu = su_m[j];
-                const float M2 = fmaxf(M[jj], mu);
-                const float ap = (M[jj] == -INFINITY) ? 0.0f : exp2f(M[jj] - M2);
-                const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
-                denom = ap * L[jj] + au * su_l[j];
+        for (int e = 0; e < FD; ++e) o[e] = fmaf(z[e], sp_, su_v[i][e] * su_);
+        const int rowi = wave + kWaves * (4 * i + fq);
+        if (rowi < R) {
+            float* out = a.out + (((uint64_t)f_agent[i] * a.lc + lj) * a.hq + f_head[i]) * D + FD * fl;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = ap * z[jj][e] * (1.0f / D) + au * su_v[j][e];
-            } else {
-                denom = L[jj];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = z[jj][e] * (1.0f / D);
-            }
-            const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
-            float* out = a.out + (((uint64_t)out_agent[j] * a.lc + lj) * a.hq + head) * D + EPL * lane;
-            if constexpr (EPL == 2) {
-                *reinterpret_cast<float2*>(out) = make_float2(o[0] * rinv, o[1] * rinv);
-            } else {
-                out[0] = o[0] * rinv;
-            }
+            for (int e4 = 0; e4 < FD; e4 += 4)
+                *reinterpret_cast<float4*>(out + e4) = make_float4(o[e4], o[e4 + 1], o[e4 + 2], o[e4 + 3]);
         }
     }
 }

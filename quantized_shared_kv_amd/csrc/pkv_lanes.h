@@ -25,4 +25,24 @@ __device__ __forceinline__ float lane_xor(float v) {
     }
 }
 
+// lane_xor_row<M>(v, lane) for M in {1, 2, 4, 8}: the value of lane (lane ^ M),
+// from DPP moves alone (no LDS-pipe swizzle).  Within a 16-lane row, row_ror:n
+// hands lane i the value of lane (i - n) mod 16; the partner at distance 4 is
+// lane i + 4 (rotation by 12) when bit 2 of i is clear and i - 4 (rotation by 4)
+// otherwise, and the one at distance 8 is lane (i + 8) mod 16 either way.
+template <int M>
+__device__ __forceinline__ float lane_xor_row(float v, int lane) {
+    const int x = __builtin_bit_cast(int, v);
+    if constexpr (M == 1 || M == 2) {
+        return lane_xor<M>(v);
+    } else if constexpr (M == 4) {
+        const int down = __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, true);  // row_ror:4  -> lane i - 4
+        const int up = __builtin_amdgcn_mov_dpp(x, 0x12C, 0xF, 0xF, true);    // row_ror:12 -> lane i + 4
+        return __builtin_bit_cast(float, (lane & 4) ? down : up);
+    } else {
+        static_assert(M == 8, "distance within a 16-lane row");
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));  // row_ror:8
+    }
+}
+
 }  // namespace pkv
