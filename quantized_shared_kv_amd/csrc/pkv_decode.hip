@@ -470,20 +470,23 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 template <int D, int RS>
 __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
-    // score sweep: LPT lanes per token, each reading KL 16-byte chunks of it
-    constexpr int LPT = (RS * D / 128) > 1 ? RS * D / 128 : 1;
+    // score sweep: LPT lanes per token, each reading KL 16-byte chunks of it (and holding the
+    // matching query slices: RS * KL * 4 registers)
+    constexpr int LPT = (RS * D / 64) > 2 ? RS * D / 64 : 2;
     constexpr int TPP = 64 / LPT;           // tokens per load instruction
     constexpr int KL = D / 8 / LPT;         // 16-byte chunks per lane per token
-    constexpr int KU = kSfxGroup / TPP;     // load instructions per chunk index per group
-    constexpr int RPL = RS / LPT;           // rows per lane after the reduce-scatter
-    constexpr int LB = LPT == 1 ? 0 : LPT == 2 ? 1 : LPT == 4 ? 2 : 3;  // log2 LPT
+    constexpr int KG = TPP > (RS >= 4 ? 16 : 32) ? TPP : (RS >= 4 ? 16 : 32);  // tokens per score group
+    constexpr int KU = KG / TPP;            // load instructions per chunk index per group
+    constexpr int RPL = RS / LPT > 1 ? RS / LPT : 1;  // rows per lane after the reduction
+    constexpr int LB = LPT == 2 ? 1 : LPT == 4 ? 2 : LPT == 8 ? 3 : 4;      // log2 LPT
+    constexpr int LS = RS / RPL == 1 ? 0 : RS / RPL == 2 ? 1 : RS / RPL == 4 ? 2 : 3;  // scatter steps
     // value sweep: LV lanes per token, 8 dimensions each
     constexpr int LV = D / 8;
     constexpr int TV = 64 / LV;             // tokens per load instruction
-    constexpr int VG = RS >= 8 ? 32 : 64;   // tokens per value group (bounds the probabilities held)
+    constexpr int VG = RS >= 4 ? 16 : 32;   // tokens per value group (bounds the probabilities held)
     constexpr int VU = VG / TV;             // load instructions per group
     constexpr int TB = TV == 4 ? 2 : 3;     // log2 TV
-    static_assert(RPL >= 1 && LPT <= 8 && (TV == 4 || TV == 8), "suffix tiling");
+    static_assert(KL >= 1 && LPT <= 16 && (1 << LS) * RPL == RS && (TV == 4 || TV == 8), "suffix tiling");
 
     const int lane = threadIdx.x & 63;
     const int g = unit % a.hkv;
@@ -498,9 +501,11 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
     const int part = lane % LPT;  // score sweep: chunks part, part + LPT, ... of token lane / LPT
     const int tl = lane / LPT;
     int rb = 0;                   // first row this lane keeps after the reduce-scatter
-    if constexpr (LB >= 1) rb += (lane & 1) * (RS / 2);
-    if constexpr (LB >= 2) rb += ((lane >> 1) & 1) * (RS / 4);
-    if constexpr (LB >= 3) rb += ((lane >> 2) & 1) * (RS / 8);
+    if constexpr (LS >= 1) rb += (lane & 1) * (RS / 2);
+    if constexpr (LS >= 2) rb += ((lane >> 1) & 1) * (RS / 4);
+    if constexpr (LS >= 3) rb += ((lane >> 2) & 1) * (RS / 8);
+    // the lane bits past the scatter steps are summed over: one lane of each copy writes
+    const bool swriter = ((lane & (LPT - 1)) >> LS) == 0;
     const int dv = lane % LV;     // value sweep: dimensions 8 dv .. 8 dv + 7 of token lane / LV
     const int tv = lane / LV;
 
@@ -541,7 +546,7 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
             float mloc[RPL];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) mloc[i] = -INFINITY;
-            for (int g0 = 0; g0 < nc; g0 += kSfxGroup) {
+            for (int g0 = 0; g0 < nc; g0 += KG) {
                 uint4 kk[KU][KL];
 #pragma unroll
                 for (int u = 0; u < KU; ++u) {
@@ -567,16 +572,23 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
                                                                         __builtin_bit_cast(bf16x2_t, qv[r][4 * c + w]),
                                                                         sc[r], false);
                     }
-                    if constexpr (LB >= 1) scatter_add<1, RS>(sc, lane & 1);
-                    if constexpr (LB >= 2) scatter_add<2, RS / 2>(sc, lane & 2);
-                    if constexpr (LB >= 3) scatter_add<4, RS / 4>(sc, lane & 4);
+                    // over lane bits 0 .. LB-1: scatter the rows while more than one is left, then sum
+                    auto red = [&](auto bt) {
+                        constexpr int b = decltype(bt)::value;
+                        if constexpr (b < LS) scatter_add<(1 << b), (RS >> b)>(sc, lane & (1 << b));
+                        else if constexpr (b < LB) all_add<(1 << b), RPL>(sc);
+                    };
+                    red(std::integral_constant<int, 0>{});
+                    red(std::integral_constant<int, 1>{});
+                    red(std::integral_constant<int, 2>{});
+                    red(std::integral_constant<int, 3>{});
                     const bool ok = t < nc;
 #pragma unroll
                     for (int i = 0; i < RPL; ++i) {
                         const float x = sc[i] * a.sm_log2;
                         if (ok) {
                             mloc[i] = fmaxf(mloc[i], x);
-                            sbuf[t * RS + rb + i] = x;
+                            if (swriter) sbuf[t * RS + rb + i] = x;
                         }
                     }
                 }
@@ -589,11 +601,11 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
             }
 #pragma unroll
             for (int r = 0; r < RS; ++r) {
-                // rows [rb, rb + RPL) sit on the lanes whose low LB bits, reversed, give rb / RPL
+                // rows [rb, rb + RPL) sit on the lanes whose low LS bits, reversed, give rb / RPL
                 const int q = r / RPL;
                 int src = 0;
 #pragma unroll
-                for (int b = 0; b < LB; ++b) src |= ((q >> (LB - 1 - b)) & 1) << b;
+                for (int b = 0; b < LS; ++b) src |= ((q >> (LS - 1 - b)) & 1) << b;
                 const float mc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mloc[r % RPL]), src));
                 const float mn = fmaxf(M[r], mc);
                 const float alpha = (M[r] == -INFINITY) ? 0.0f : exp2f(M[r] - mn);
