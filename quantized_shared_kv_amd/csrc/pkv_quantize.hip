@@ -154,38 +154,117 @@ __device__ __forceinline__ void butterfly(float (&z)[kGroupTokens][EPL], int lan
         for (int e = 0; e < EPL; ++e) z[i][e] = __builtin_fmaf(sgn, z[i][e], lane_xor<M>(z[i][e]));
 }
 
+// Raw K and V of one 8-token group for this lane: its EPL elements of each token, as
+// stored (bf16 bit patterns, or fp32 bits), 0 for tokens outside the append.
+template <int EPL, bool BF16>
+struct EncRaw {
+    static constexpr int W = BF16 ? (EPL + 1) / 2 : EPL;  // 32-bit words per token per tensor
+    uint32_t k[kGroupTokens][W], v[kGroupTokens][W];
+};
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ void enc_load(const EncodeArgs& a, int grp, int g, int j, EncRaw<EPL, BF16>& r) {
+    constexpr int D = 64 * EPL;
+    const int lane = threadIdx.x & 63;
+    const int gt0 = grp * kGroupTokens;
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        const bool valid = gt0 + i >= a.t0 && gt0 + i < a.t0 + a.n;
+        const uint64_t src = (((uint64_t)j * a.hkv + g) * a.n + (valid ? gt0 + i - a.t0 : 0)) * D + EPL * lane;
+        if constexpr (BF16 && EPL == 2) {  // one dword: the lane's two bf16 values
+            r.k[i][0] = valid ? static_cast<const uint32_t*>(a.k)[src / 2] : 0u;
+            r.v[i][0] = valid ? static_cast<const uint32_t*>(a.v)[src / 2] : 0u;
+        } else if constexpr (BF16) {
+            r.k[i][0] = valid ? static_cast<const uint16_t*>(a.k)[src] : 0u;
+            r.v[i][0] = valid ? static_cast<const uint16_t*>(a.v)[src] : 0u;
+        } else if constexpr (EPL == 2) {
+            const uint2 kk = valid ? static_cast<const uint2*>(a.k)[src / 2] : make_uint2(0u, 0u);
+            const uint2 vv = valid ? static_cast<const uint2*>(a.v)[src / 2] : make_uint2(0u, 0u);
+            r.k[i][0] = kk.x;
+            r.k[i][EPL - 1] = kk.y;
+            r.v[i][0] = vv.x;
+            r.v[i][EPL - 1] = vv.y;
+        } else {
+            r.k[i][0] = valid ? static_cast<const uint32_t*>(a.k)[src] : 0u;
+            r.v[i][0] = valid ? static_cast<const uint32_t*>(a.v)[src] : 0u;
+        }
+    }
+}
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ float enc_elem(const uint32_t (&w)[EncRaw<EPL, BF16>::W], int e) {
+    if constexpr (BF16 && EPL == 2) return __uint_as_float(e == 0 ? w[0] << 16 : w[0] & 0xffff0000u);
+    else if constexpr (BF16) return __uint_as_float(w[0] << 16);
+    else return __uint_as_float(w[e]);
+}
+
+// c ? x : y on register values: the empty asm hands the select values rather than the
+// table's elements, so the compiler does not turn it into an indexed load of the table
+__device__ __forceinline__ float sel(bool c, float x, float y) {
+    asm("" : "+v"(x), "+v"(y));
+    return c ? x : y;
+}
+
+// Lloyd-Max code of y: the number of thresholds t[0] < ... < t[2^BITS - 2] strictly below
+// y, found by a binary search over the sorted table (each level one comparison; the
+// threshold of the next level picked by the bits found so far).
+template <int BITS>
+__device__ __forceinline__ uint32_t lm_code(float y, const float* t) {
+    if constexpr (BITS == 2) {
+        const bool b1 = y > t[1];
+        const bool b0 = y > sel(b1, t[2], t[0]);
+        return (b1 ? 2u : 0u) + (b0 ? 1u : 0u);
+    } else if constexpr (BITS == 3) {
+        const bool b2 = y > t[3];
+        const bool b1 = y > sel(b2, t[5], t[1]);
+        const float u0 = sel(b1, t[2], t[0]), u1 = sel(b1, t[6], t[4]);
+        const bool b0 = y > sel(b2, u1, u0);
+        return (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (b0 ? 1u : 0u);
+    } else {
+        const bool b3 = y > t[7];
+        const bool b2 = y > sel(b3, t[11], t[3]);
+        const bool b1 = y > sel(b3, sel(b2, t[13], t[9]), sel(b2, t[5], t[1]));
+        const float u0 = sel(b1, t[2], t[0]), u1 = sel(b1, t[6], t[4]), u2 = sel(b1, t[10], t[8]),
+                    u3 = sel(b1, t[14], t[12]);
+        const bool b0 = y > sel(b3, sel(b2, u3, u2), sel(b2, u1, u0));
+        return (b3 ? 8u : 0u) + (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (b0 ? 1u : 0u);
+    }
+}
+
 // One wavefront encodes one 8-token code group of one (layer, kv head); the 8
 // tokens are processed together so their cross-lane reductions and butterflies
 // are independent and overlap.  Lane lam holds dimensions EPL*lam .. EPL*lam + EPL-1.
-template <int EPL, int BITS>
-__device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t* stage, float& nmax) {
+template <int EPL, int BITS, bool BF16>
+__device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g, int j, const EncRaw<EPL, BF16>& raw,
+                             uint8_t* stage, float& nmax) {
 #pragma clang fp contract(off)
     constexpr int D = 64 * EPL;
-    constexpr int NT = (1 << BITS) - 1;
     const int lane = threadIdx.x & 63;
     const int l = a.l0 + j;
-    const float* thr = a.thr[BITS - 2];
+    float thr[(1 << BITS) - 1];
+#pragma unroll
+    for (int k = 0; k < (1 << BITS) - 1; ++k) thr[k] = a.thr[BITS - 2][k];
 
     const float amax = __uint_as_float(reinterpret_cast<const uint32_t*>(a.base + a.off_amax)[l]);
     const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
+    const float rs = s > 0.0f ? 1.0f / s : 0.0f;
 
     const int gt0 = grp * kGroupTokens;
     bool valid[kGroupTokens];
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) valid[i] = gt0 + i >= a.t0 && gt0 + i < a.t0 + a.n;
 
-    // ---- loads (K and V of the group's tokens in this append)
     float kx[kGroupTokens][EPL], vx[kGroupTokens][EPL];
 #pragma unroll
-    for (int i = 0; i < kGroupTokens; ++i) {
-        const uint64_t src = (((uint64_t)j * a.hkv + g) * a.n + (valid[i] ? gt0 + i - a.t0 : 0)) * D + EPL * lane;
+    for (int i = 0; i < kGroupTokens; ++i)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            kx[i][e] = valid[i] ? load_elem(a.k, a.dtype, src + e) : 0.0f;
-            vx[i][e] = valid[i] ? load_elem(a.v, a.dtype, src + e) : 0.0f;
+            kx[i][e] = enc_elem<EPL, BF16>(raw.k[i], e);
+            vx[i][e] = enc_elem<EPL, BF16>(raw.v[i], e);
         }
-    }
-    // ---- K rows: q = clamp(rint(k / s), -127, 127)
+    // ---- K rows: q = clamp(rint(k / s), -127, 127).  k * (1/s) is within 1.5e-5 of the
+    // correctly rounded quotient (|k / s| <= 127), so it rounds the same way unless it lies
+    // within 3e-5 of a half-integer; only then is the quotient itself computed.
     int8_t* kq = reinterpret_cast<int8_t*>(a.base + a.off_kq) + ((uint64_t)l * a.hkv + g) * a.tc * D;
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) {
@@ -194,7 +273,13 @@ __device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             float q = 0.0f;
-            if (s > 0.0f) q = fminf(fmaxf(rintf(kx[i][e] / s), -127.0f), 127.0f);
+            if (s > 0.0f) {
+                const float t = kx[i][e] * rs;
+                const float fr = t - floorf(t);
+                q = rintf(t);
+                if (fabsf(fr - 0.5f) < 3.0e-5f) q = rintf(kx[i][e] / s);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            }
             packed |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(static_cast<int>(q)))) << (8 * e);
         }
         if (EPL == 2)
@@ -214,12 +299,22 @@ __device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t
     tree_level<4>(sq);
     tree_level<2>(sq);
     tree_level<1>(sq);
-    float nrm[kGroupTokens];
+    // every lane now holds the 8 sums; lane i < 8 takes the square root and reciprocal of
+    // token i's, and the wave reads them back from those lanes
+    float mine = 0.0f;
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) {
         float ss = sq[i][0];
         if (EPL == 2) ss = sq[i][0] + sq[i][EPL - 1];
-        nrm[i] = sqrtf(ss);
+        mine = lane == i ? ss : mine;
+    }
+    const float n_l = sqrtf(mine);
+    const float r_l = n_l > 0.0f ? 1.0f / n_l : 0.0f;
+    float nrm[kGroupTokens], rcp[kGroupTokens];
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        nrm[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(n_l), i));
+        rcp[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_l), i));
     }
     // ---- FWHT, ascending half-width (the in-lane stage first when EPL == 2)
     if (EPL == 2) {
@@ -236,22 +331,15 @@ __device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t
     butterfly<8>(vx, lane);
     butterfly<16>(vx, lane);
     butterfly<32>(vx, lane);
-    // ---- codes: number of thresholds strictly below y = z * (1/n); 8 tokens per field
+    // ---- codes of y = z * (1/n); 8 tokens per field
     uint32_t field[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) field[e] = 0u;
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) {
         if (!valid[i] || !(nrm[i] > 0.0f)) continue;
-        const float r = 1.0f / nrm[i];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float y = vx[i][e] * r;
-            uint32_t c = 0;
-#pragma unroll
-            for (int k = 0; k < NT; ++k) c += (y > thr[k]) ? 1u : 0u;
-            field[e] |= c << (BITS * i);
-        }
+        for (int e = 0; e < EPL; ++e) field[e] |= lm_code<BITS>(vx[i][e] * rcp[i], thr) << (BITS * i);
         nmax = fmaxf(nmax, nrm[i]);
     }
     uint8_t* vc = a.base + a.off_vc[j] + ((uint64_t)g * (a.tc / kGroupTokens) + grp) * (uint64_t)(D * BITS);
@@ -268,16 +356,11 @@ __device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t
     // ---- norms and scales of the valid tokens: lane i < 8 stores token i
     float* vn = reinterpret_cast<float*>(a.base + a.off_vn) + ((uint64_t)l * a.hkv + g) * a.tc;
     float* ks = reinterpret_cast<float*>(a.base + a.off_ks) + (uint64_t)l * a.tc;
-    float mine = 0.0f;
     bool mine_ok = false;
 #pragma unroll
-    for (int i = 0; i < kGroupTokens; ++i)
-        if (lane == i) {
-            mine = nrm[i];
-            mine_ok = valid[i];
-        }
+    for (int i = 0; i < kGroupTokens; ++i) mine_ok = lane == i ? valid[i] : mine_ok;
     if (lane < kGroupTokens && mine_ok) {
-        vn[gt0 + lane] = mine;
+        vn[gt0 + lane] = n_l;
         if (g == 0) ks[gt0 + lane] = s;
     }
     // ---- code fields: dimension dim -> bytes [dim*BITS, dim*BITS + BITS), staged in LDS
@@ -293,9 +376,10 @@ __device__ void encode_group(const EncodeArgs& a, int grp, int g, int j, uint8_t
     __builtin_amdgcn_wave_barrier();
 }
 
-// grid (ceil(groups / kGroupsPerWg), hkv, nl), 256 threads
-template <int EPL, int BITS>
-__device__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
+// grid (ceil(groups / kGroupsPerWg), hkv, nl), 256 threads; each wavefront loads its next
+// group while it encodes the current one
+template <int EPL, int BITS, bool BF16>
+__device__ __forceinline__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
     __shared__ __align__(16) uint8_t stage[kEncWaves][128 * 4];
     __shared__ float wmax[kEncWaves];
     const int wave = threadIdx.x >> 6;
@@ -303,8 +387,17 @@ __device__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
     float nmax = 0.0f;
     const int gb = blockIdx.x * kGroupsPerWg;
     const int ge = min(n_grp, gb + kGroupsPerWg);
-    for (int gi = gb + wave; gi < ge; gi += kEncWaves)
-        encode_group<EPL, BITS>(a, grp_first + gi, g, j, stage[wave], nmax);
+    if (gb + wave < ge) {
+        EncRaw<EPL, BF16> cur;
+        enc_load<EPL, BF16>(a, grp_first + gb + wave, g, j, cur);
+        for (int gi = gb + wave; gi < ge; gi += kEncWaves) {
+            // the last group loads itself again rather than branching around the load
+            EncRaw<EPL, BF16> nxt;
+            enc_load<EPL, BF16>(a, grp_first + min(gi + kEncWaves, ge - 1), g, j, nxt);
+            encode_group<EPL, BITS, BF16>(a, grp_first + gi, g, j, cur, stage[wave], nmax);
+            cur = nxt;
+        }
+    }
     if ((threadIdx.x & 63) == 0) wmax[wave] = nmax;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -314,17 +407,23 @@ __device__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
     }
 }
 
-__global__ void __launch_bounds__(256) k_encode(EncodeArgs a, int grp_first, int n_grp) {
+template <bool BF16>
+__device__ __forceinline__ void encode_dispatch(const EncodeArgs& a, int grp_first, int n_grp) {
     const int b = a.bits[blockIdx.z];
     if (a.d == 128) {
-        if (b == 2) encode_wg<2, 2>(a, grp_first, n_grp);
-        else if (b == 3) encode_wg<2, 3>(a, grp_first, n_grp);
-        else encode_wg<2, 4>(a, grp_first, n_grp);
+        if (b == 2) encode_wg<2, 2, BF16>(a, grp_first, n_grp);
+        else if (b == 3) encode_wg<2, 3, BF16>(a, grp_first, n_grp);
+        else encode_wg<2, 4, BF16>(a, grp_first, n_grp);
     } else {
-        if (b == 2) encode_wg<1, 2>(a, grp_first, n_grp);
-        else if (b == 3) encode_wg<1, 3>(a, grp_first, n_grp);
-        else encode_wg<1, 4>(a, grp_first, n_grp);
+        if (b == 2) encode_wg<1, 2, BF16>(a, grp_first, n_grp);
+        else if (b == 3) encode_wg<1, 3, BF16>(a, grp_first, n_grp);
+        else encode_wg<1, 4, BF16>(a, grp_first, n_grp);
     }
+}
+
+__global__ void __launch_bounds__(256) k_encode(EncodeArgs a, int grp_first, int n_grp) {
+    if (a.dtype == PKV_BF16) encode_dispatch<true>(a, grp_first, n_grp);
+    else encode_dispatch<false>(a, grp_first, n_grp);
 }
 
 }  // namespace
