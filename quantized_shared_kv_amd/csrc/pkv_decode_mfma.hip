@@ -155,16 +155,16 @@ struct Chunk {
 // compile-time) in this lane's copy: field * kLutCopies * 4 + lane_base.  The field
 // is shifted straight into place and masked; with the LUT 32 KB-aligned, the sum
 // with lane_base (< 128 above the LUT) has disjoint bits.
-template <int NBYTES, int P, int W>
+template <int NBYTES, int P, int W, int ES = 7>
 __device__ __forceinline__ uint32_t lut_offset(const Chunk<NBYTES>& c, uint32_t lane_base) {
     constexpr int wi = P >> 5, sh = P & 31;
-    constexpr uint32_t mask = ((1u << W) - 1u) << 7;  // kLutCopies * 4 = 128 bytes per entry
+    constexpr uint32_t mask = ((1u << W) - 1u) << ES;  // entries of 2^ES bytes (pairs: kLutCopies * 4)
     uint32_t x;
     if constexpr (sh + W <= 32) {
-        if constexpr (sh >= 7) x = (c.w[wi] >> (sh - 7)) & mask;
-        else x = (c.w[wi] << (7 - sh)) & mask;
+        if constexpr (sh >= ES) x = (c.w[wi] >> (sh - ES)) & mask;
+        else x = (c.w[wi] << (ES - sh)) & mask;
     } else {
-        x = (__builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh) << 7) & mask;
+        x = (__builtin_amdgcn_alignbit(c.w[wi + 1], c.w[wi], sh) << ES) & mask;
     }
     return x + lane_base;
 }
@@ -175,13 +175,30 @@ __device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, uint32_t la
     return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(off));
 }
 
+// 3-bit codes: one 8-byte entry per 4 codes (a 12-bit field), a single copy of 4096
+// entries at the start of LDS, so the offset is the field times 8
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int NBYTES, int NBI, int QI>
+__device__ __forceinline__ u32x2 lut_quad(const Chunk<NBYTES>& c, uint32_t lut_base) {
+    const uint32_t off = lut_offset<NBYTES, 24 * NBI + 12 * QI, 12, 3>(c, lut_base);
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(static_cast<uintptr_t>(off));
+}
+
 template <int NBYTES, int BITS, int NBI>
 __device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, uint32_t lane_base) {
     H8 r;
-    r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lane_base);
-    r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lane_base);
-    r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lane_base);
-    r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lane_base);
+    if constexpr (BITS == 3) {
+        const u32x2 q0 = lut_quad<NBYTES, NBI, 0>(c, lane_base), q1 = lut_quad<NBYTES, NBI, 1>(c, lane_base);
+        r.u[0] = q0.x;
+        r.u[1] = q0.y;
+        r.u[2] = q1.x;
+        r.u[3] = q1.y;
+    } else {
+        r.u[0] = lut_pair<NBYTES, BITS, NBI, 0>(c, lane_base);
+        r.u[1] = lut_pair<NBYTES, BITS, NBI, 1>(c, lane_base);
+        r.u[2] = lut_pair<NBYTES, BITS, NBI, 2>(c, lane_base);
+        r.u[3] = lut_pair<NBYTES, BITS, NBI, 3>(c, lane_base);
+    }
     return r.h;
 }
 
@@ -492,8 +509,18 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         sum += __shfl_xor(sum, 32, 64);
         qoff[rt] = -1152.0f * sum;
     }
-    // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
-    {
+    if constexpr (BITS == 3) {
+        // LUT of fp16 centroid quads: entry e = c0 | c1 << 3 | c2 << 6 | c3 << 9 ->
+        // (c[c0], c[c1], c[c2], c[c3]); this thread's entries tid + 256 k share the low pair
+        const uint32_t lo = pack_h2(__shfl(cl, tid & 7, 64), __shfl(cl, (tid >> 3) & 7, 64));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int hp = (tid >> 6) + 4 * k;  // the entry's high pair, c2 | c3 << 3
+            const uint32_t hi = pack_h2(__shfl(cl, hp & 7, 64), __shfl(cl, hp >> 3, 64));
+            reinterpret_cast<uint2*>(g_big.loop.lut)[tid + 256 * k] = make_uint2(lo, hi);
+        }
+    } else {
+        // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
         constexpr int NE = 1 << (2 * BITS);
 #pragma unroll
         for (int i0 = 0; i0 < NE * kLutCopies; i0 += 256) {
@@ -505,7 +532,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
     lds_barrier();  // LUT and query operands ready
 
-    const uint32_t lut_lane = lds_addr(g_big.loop.lut) + 4u * (lane & (kLutCopies - 1));  // this lane's LUT copy
+    // this lane's LUT copy (pairs), or the single quad table (3-bit)
+    const uint32_t lut_lane = lds_addr(g_big.loop.lut) + (BITS == 3 ? 0u : 4u * (lane & (kLutCopies - 1)));
     const uint32_t ring_a = lds_addr(ring);
     const float fs = a.sm_log2;
 
