@@ -177,18 +177,20 @@ __device__ __forceinline__ uint32_t lut_pair(const Chunk<NBYTES>& c, uint32_t la
 
 // 3-bit codes: one 8-byte entry per 4 codes (a 12-bit field), a single copy of 4096
 // entries at the start of LDS, so the offset is the field times 8
+// 2-bit codes: 256 entries of 4 codes (an 8-bit field) in 16 copies, 128 bytes per entry
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-template <int NBYTES, int NBI, int QI>
+template <int NBYTES, int BITS, int NBI, int QI>
 __device__ __forceinline__ u32x2 lut_quad(const Chunk<NBYTES>& c, uint32_t lut_base) {
-    const uint32_t off = lut_offset<NBYTES, 24 * NBI + 12 * QI, 12, 3>(c, lut_base);
+    constexpr int W = 4 * BITS;
+    const uint32_t off = lut_offset<NBYTES, 8 * BITS * NBI + W * QI, W, BITS == 3 ? 3 : 7>(c, lut_base);
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(static_cast<uintptr_t>(off));
 }
 
 template <int NBYTES, int BITS, int NBI>
 __device__ __forceinline__ half8 decode_b(const Chunk<NBYTES>& c, uint32_t lane_base) {
     H8 r;
-    if constexpr (BITS == 3) {
-        const u32x2 q0 = lut_quad<NBYTES, NBI, 0>(c, lane_base), q1 = lut_quad<NBYTES, NBI, 1>(c, lane_base);
+    if constexpr (BITS <= 3) {
+        const u32x2 q0 = lut_quad<NBYTES, BITS, NBI, 0>(c, lane_base), q1 = lut_quad<NBYTES, BITS, NBI, 1>(c, lane_base);
         r.u[0] = q0.x;
         r.u[1] = q0.y;
         r.u[2] = q1.x;
@@ -519,6 +521,16 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             const uint32_t hi = pack_h2(__shfl(cl, hp & 7, 64), __shfl(cl, hp >> 3, 64));
             reinterpret_cast<uint2*>(g_big.loop.lut)[tid + 256 * k] = make_uint2(lo, hi);
         }
+    } else if constexpr (BITS == 2) {
+        // 16 copies of the 256 quads: slot tid + 256 k holds entry (tid >> 4) + 16 k, whose
+        // low pair (tid >> 4) & 15 is this thread's for every k
+        const int lp = (tid >> 4) & 15;
+        const uint32_t lo = pack_h2(__shfl(cl, lp & 3, 64), __shfl(cl, lp >> 2, 64));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t hi = pack_h2(__shfl(cl, k & 3, 64), __shfl(cl, k >> 2, 64));
+            reinterpret_cast<uint2*>(g_big.loop.lut)[tid + 256 * k] = make_uint2(lo, hi);
+        }
     } else {
         // LUT of fp16 centroid pairs: entry e = c0 | c1 << BITS -> (c[c0], c[c1])
         constexpr int NE = 1 << (2 * BITS);
@@ -532,8 +544,9 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
     lds_barrier();  // LUT and query operands ready
 
-    // this lane's LUT copy (pairs), or the single quad table (3-bit)
-    const uint32_t lut_lane = lds_addr(g_big.loop.lut) + (BITS == 3 ? 0u : 4u * (lane & (kLutCopies - 1)));
+    // this lane's LUT copy (pairs of 4-bit codes, quads of 2-bit ones), or the single 3-bit quad table
+    const uint32_t lut_lane = lds_addr(g_big.loop.lut) +
+                              (BITS == 3 ? 0u : BITS == 2 ? 8u * (lane & 15) : 4u * (lane & (kLutCopies - 1)));
     const uint32_t ring_a = lds_addr(ring);
     const float fs = a.sm_log2;
 
