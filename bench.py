@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--kernel", default="default", choices=["default", "valu", "mfma"])
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per job (default: workload's 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--private-tokens", type=int, default=0,
+                    help="give every agent a private compressed segment of this many older tokens "
+                         "(quantized in each job, attended with the shared pool and the native window)")
     ap.add_argument("--cold-calls", type=int, default=8,
                     help="extra untimed pool-kernel launches, each after a 512 MiB cache flush")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -161,7 +164,23 @@ def main():
     pool = pk.pool_build(cfg, pool_buf.data_ptr(), nbytes)
     pools = [pool] * A
     pk.pool_quantize_append(pool, 0, k_pool, v_pool)  # the workspace plan depends on the pool's token count
-    ws_bytes = pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A, kernel=kernel)
+    # optional per-agent private segments: synthetic bf16 K/V of the same scale, seeded on the device
+    NP = args.private_tokens
+    prv_pools, prv_bufs, prv_cfg, prv_kv = None, [], None, None
+    if NP > 0:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        prv_cfg = pk.make_config(L, Hkv, d, NP, w.v_bits(0))
+        pb = pk.pool_bytes(prv_cfg)
+        prv_kv = [(torch.randn((L, Hkv, NP, d), generator=gen, device=dev).to(torch.bfloat16),
+                   torch.randn((L, Hkv, NP, d), generator=gen, device=dev).to(torch.bfloat16)) for _ in range(A)]
+        prv_pools = []
+        for a in range(A):
+            prv_bufs.append(torch.empty(pb, dtype=torch.uint8, device=dev))
+            prv_pools.append(pk.pool_build(prv_cfg, prv_bufs[-1].data_ptr(), pb))
+            pk.pool_quantize_append(prv_pools[a], 0, *prv_kv[a])
+    ws_bytes = pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A, kernel=kernel,
+                                         private_pools=prv_pools)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in {time.time() - t0:.1f}s; pool {nbytes / 1e6:.1f} MB, workspace "
@@ -181,12 +200,18 @@ def main():
         if timed_kernels:
             b0.record()
         pk.pool_quantize_append(pool, 0, k_pool, v_pool)
+        if prv_pools is not None:
+            for a in range(A):
+                fresh = pk.pool_build(prv_cfg, prv_bufs[a].data_ptr(), prv_bufs[a].numel())
+                for f in pk.Pool._fields_:
+                    setattr(prv_pools[a], f[0], getattr(fresh, f[0]))
+                pk.pool_quantize_append(prv_pools[a], 0, *prv_kv[a])
         if timed_kernels:
             b1.record()
         for s in range(steps_per_job):
             lens = [min(s + 1, S)] * A
             pk.agent_decode_attention(pools, q_all[s], out, 0, sfx_k, sfx_v, lens, workspace=ws, kernel=kernel,
-                                      pool_events=evs[s] if timed_kernels else None)
+                                      pool_events=evs[s] if timed_kernels else None, private_pools=prv_pools)
 
     for i in range(args.warmup):
         one_job(False)
@@ -215,7 +240,7 @@ def main():
     for i in range(args.cold_calls):
         scratch.fill_(i & 255)
         pk.agent_decode_attention(pools, q_all[i % steps_per_job], out, 0, sfx_k, sfx_v, [S] * A, workspace=ws,
-                                  kernel=kernel, pool_events=evs[0])
+                                  kernel=kernel, pool_events=evs[0], private_pools=prv_pools)
         torch.cuda.synchronize()
         cold_ms.append(evs[0][0].elapsed_time(evs[0][1]))
     del scratch
@@ -225,6 +250,7 @@ def main():
     # the bf16 queries read and the fp32 outputs written
     bits = 3
     pool_alg = L * Hkv * T * (d + d * bits // 8 + 4) + L * T * 4
+    pool_alg += A * (L * Hkv * NP * (d + d * bits // 8 + 4) + L * NP * 4)  # private segments, if any
     q_bytes = A * L * Hq * d * 2
     out_bytes = A * L * Hq * d * 4
     alg = pool_alg + q_bytes + out_bytes
@@ -235,7 +261,7 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             t = json.load(open(args.traffic_json))
-            if (t.get("kernel_variant") == variant and t.get("workload") == w.name
+            if (NP == 0 and t.get("kernel_variant") == variant and t.get("workload") == w.name
                     and t.get("kernel_source_sha256") == kernel_source_sha256()):
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -255,7 +281,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "agents": A, "decode_steps_per_step": steps_per_job, "pool_tokens": T,
                    "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "v_bits": 3,
-                   "suffix": f"bf16, s+1 tokens at decode step s (max {S})", "kernel": args.kernel},
+                   "suffix": f"bf16, s+1 tokens at decode step s (max {S})", "kernel": args.kernel,
+                   **({"private_tokens_per_agent": NP} if NP else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "pool decode", "alg_bytes_per_launch": alg, "avg_launch_us": avg_pool_ms * 1e3,

@@ -155,6 +155,11 @@ typedef struct {
     void* const* pool_events;         /* optional instrumentation: NULL, or two hipEvent_t recorded on
                                          the stream right before the first and right after the last
                                          pool-kernel launch of the call */
+    const pkv_pool* const* agent_private_pool;
+                                      /* optional, host [n_agents]: NULL, or per agent NULL or a second
+                                         pool the agent alone (or every agent naming it) also attends:
+                                         its own older tokens, quantized once when they left the
+                                         native window (pool_quantize_append on that pool) */
 } pkv_decode_args;
 
 #define PKV_KERNEL_DEFAULT 0
@@ -168,9 +173,12 @@ typedef struct {
  * pool; section 2.B: V is dequantised by centroid lookup and inverse FWHT.
  *
  * For agent a, layer l, query head h (kv head g = h / (n_q_heads/n_kv_heads)):
- *   o = softmax(sigma * q . [K_hat; K_sfx]) @ [V_hat; V_sfx]
+ *   o = softmax(sigma * q . [K_hat; K_prv; K_sfx]) @ [V_hat; V_prv; V_sfx]
  * with K_hat = Ks * Kq and V_hat = (Vn / d) * H @ c[code] over the pool's
- * tokens, and the first sfx_len[a] suffix tokens; no mask.  Each pool byte is
+ * tokens, K_prv / V_prv the same over the agent's private pool when one is
+ * given (CoMixKV news article, incremental quantization: recent tokens stay
+ * native, older ones are quantized once and never rewritten), and the first
+ * sfx_len[a] suffix tokens; no mask.  Each pool byte is
  * read once per call for all agents that share the pool (their query heads
  * are batched), V is accumulated in the rotated domain and one inverse FWHT
  * is applied per output.  fp32 accumulation.
@@ -179,8 +187,9 @@ typedef struct {
  * Call with workspace == NULL to have the required size written to
  * *workspace_bytes (nothing enqueued); PKV_ENOSPACE if the given size is too
  * small.  The size depends only on the call's shapes and the split plan.
- * All agents' pools must share n_kv_heads and head_dim, hold the layers of the
- * call, and hold the same token count in each of those layers.  q, out,
+ * All agents' pools, private pools included, must share n_kv_heads and
+ * head_dim, hold the layers of the call, and hold the same token count in
+ * each of those layers (a private pool may hold none).  q, out,
  * sfx_k and sfx_v must be 16-byte aligned (PKV_EINVAL otherwise).
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOSPACE, PKV_EHIP.
  */

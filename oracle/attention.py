@@ -10,7 +10,11 @@ details, so standard decode attention is used):
   pool token and every token of its own suffix);
 * grouped-query attention maps q head h to kv head floor(h / G), G = Hq / Hkv
   (contiguous groups);
-* o = softmax(sigma * q . [K_hat; K_sfx]) @ [V_hat; V_sfx], all in fp64.
+* o = softmax(sigma * q . [K_hat; K_sfx]) @ [V_hat; V_sfx], all in fp64;
+* an agent with a private compressed segment (its own older tokens, quantized
+  once when they left the native window: the incremental quantization the
+  CoMixKV article describes) attends to the shared pool, then that segment,
+  then its native suffix: the three token sets are concatenated.
 
 ``rotated_form`` writes the same output the way the GPU accumulates it: the
 pool part of the value sum stays in the rotated, normalised domain,
@@ -78,7 +82,8 @@ def rotated_form(q, k_scale, k_codes, v_norm, v_codes, bits, k_sfx=None, v_sfx=N
     return o / l
 
 
-def decode_call(queries, pool_of_agent, decoded, k_sfx, v_sfx, sfx_len, n_kv_heads, sigma=None):
+def decode_call(queries, pool_of_agent, decoded, k_sfx, v_sfx, sfx_len, n_kv_heads, sigma=None,
+                private=None):
     """Outputs of one decode call for every (agent, layer, q head), fp64.
 
     queries    [A][L][Hq][d] query values
@@ -86,6 +91,8 @@ def decode_call(queries, pool_of_agent, decoded, k_sfx, v_sfx, sfx_len, n_kv_hea
     decoded    callable (pool, layer, kv_head) -> (K_hat [T][d], V_hat [T][d])
     k_sfx, v_sfx  callables (agent, layer) -> [Hkv][S_cap][d] native suffix values (or None)
     sfx_len[a] suffix tokens agent a attends to
+    private    optional callable (agent, layer, kv_head) -> (K_hat, V_hat) of the agent's
+               private segment, or None for an agent without one
     Returns [A][L][Hq][d].
     """
     q = np.asarray(queries, dtype=np.float64)
@@ -100,6 +107,10 @@ def decode_call(queries, pool_of_agent, decoded, k_sfx, v_sfx, sfx_len, n_kv_hea
                 vs = v_sfx(a, l)
             for g in range(n_kv_heads):
                 khat, vhat = decoded(pool_of_agent[a], l, g)
+                seg = private(a, l, g) if private is not None else None
+                if seg is not None:
+                    khat = np.concatenate([np.asarray(khat, dtype=np.float64), np.asarray(seg[0], dtype=np.float64)])
+                    vhat = np.concatenate([np.asarray(vhat, dtype=np.float64), np.asarray(seg[1], dtype=np.float64)])
                 kk = None if ks is None else ks[g, :sfx_len[a]]
                 vv = None if vs is None else vs[g, :sfx_len[a]]
                 out[a, l, g * G:(g + 1) * G] = attend_pool_and_suffix(q[a, l, g * G:(g + 1) * G], khat, vhat,

@@ -34,6 +34,8 @@ struct DecodeLaunch {
     int16_t agent_id[kMaxAgentsPerLaunch];    // call-level agent index of each launch agent
     int16_t agent_pool[kMaxAgentsPerLaunch];  // pool entry of each launch agent
     int16_t agent_pos[kMaxAgentsPerLaunch];   // index of the agent among its pool's agents
+    int16_t agent_pool2[kMaxAgentsPerLaunch]; // private pool entry of each launch agent, -1 for none
+    int16_t agent_pos2[kMaxAgentsPerLaunch];  // index of the agent among its private pool's agents
     int32_t sfx_len[kMaxAgentsPerLaunch];
     const void* q;
     const void* sfx_k;
@@ -48,6 +50,7 @@ struct DecodeLaunch {
     int32_t sfx_cap;
     int32_t has_sfx;
     int32_t fused;          // the pool kernel finishes the outputs itself (one split everywhere)
+    int32_t has_private;    // some agent also attends a private pool (outputs merged by k_merge)
     float sm_log2;          // softmax scale * log2(e)
 };
 

@@ -747,23 +747,41 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     const int h = row % a.hq;
     const int lj = (row / a.hq) % a.lc;
     const int k = row / ((uint64_t)a.hq * a.lc);
-    const PoolEntry& P = a.pools[a.agent_pool[k]];
     const int g = h / a.G;
-    const int rho = a.agent_pos[k] * a.G + h % a.G;
-    const float* rec0 = a.part + P.part_off + ((((uint64_t)lj * a.hkv + g) * P.splits) * P.rows + rho) * (2 + D);
-    const uint64_t stride = (uint64_t)P.rows * (2 + D);
+    // the agent's pool and, if it has one, its private pool: split records of both, all in
+    // the rotated domain, merged before the one inverse transform
+    const int np = a.agent_pool2[k] >= 0 ? 2 : 1;
+    auto records = [&](int which, const float*& rec0, uint64_t& stride, int& splits) {
+        const PoolEntry& P = a.pools[which == 0 ? a.agent_pool[k] : a.agent_pool2[k]];
+        const int rho = (which == 0 ? a.agent_pos[k] : a.agent_pos2[k]) * a.G + h % a.G;
+        rec0 = a.part + P.part_off + ((((uint64_t)lj * a.hkv + g) * P.splits) * P.rows + rho) * (2 + D);
+        stride = (uint64_t)P.rows * (2 + D);
+        splits = P.splits;
+    };
     float M = -INFINITY;
-    for (int s = 0; s < P.splits; ++s) M = fmaxf(M, rec0[s * stride]);
+    for (int w = 0; w < np; ++w) {
+        const float* rec0;
+        uint64_t stride;
+        int splits;
+        records(w, rec0, stride, splits);
+        for (int s = 0; s < splits; ++s) M = fmaxf(M, rec0[s * stride]);
+    }
     float L = 0.0f, z[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
     if (M != -INFINITY) {
-        for (int s = 0; s < P.splits; ++s) {
-            const float* r = rec0 + s * stride;
-            const float w = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
-            L += w * r[1];
+        for (int w = 0; w < np; ++w) {
+            const float* rec0;
+            uint64_t stride;
+            int splits;
+            records(w, rec0, stride, splits);
+            for (int s = 0; s < splits; ++s) {
+                const float* r = rec0 + s * stride;
+                const float wt = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
+                L += wt * r[1];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) z[e] += w * r[2 + EPL * lane + e];
+                for (int e = 0; e < EPL; ++e) z[e] += wt * r[2 + EPL * lane + e];
+            }
         }
     }
     // inverse transform: H z / D (lane holds dims EPL*lane + e)
@@ -816,6 +834,9 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
     const int hkv = p0->cfg.n_kv_heads, d = p0->cfg.head_dim;
     const int G = x->n_q_heads / hkv;
     const float sigma = x->softmax_scale != 0.0f ? x->softmax_scale : 1.0f / std::sqrt((float)d);
+    auto private_of = [&](int a) -> const pkv_pool* {
+        return x->agent_private_pool ? x->agent_private_pool[a] : nullptr;
+    };
 
     // group agents by pool (first appearance order)
     std::vector<const pkv_pool*> order;
@@ -825,13 +846,37 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
         if (!members.count(p)) order.push_back(p);
         members[p].push_back(a);
     }
-    // pool chunks of at most kMaxAgentsPerLaunch agents
-    struct Chunk { const pkv_pool* pool; std::vector<int> agents; };
+    // chunks of one pool's agents: at most kMaxAgentsPerLaunch agents and kMaxPoolsPerLaunch - 1
+    // distinct private pools; within a chunk the agents of one private pool are consecutive
+    // (agents without one first), so every pool entry's rows belong to consecutive launch agents
+    struct Chunk {
+        const pkv_pool* pool;
+        std::vector<int> agents;
+        std::vector<const pkv_pool*> privs;  // distinct private pools, first appearance order
+    };
     std::vector<Chunk> chunks;
     for (const pkv_pool* p : order) {
         const std::vector<int>& m = members[p];
-        for (size_t i = 0; i < m.size(); i += kMaxAgentsPerLaunch)
-            chunks.push_back({p, std::vector<int>(m.begin() + i, m.begin() + std::min(m.size(), i + kMaxAgentsPerLaunch))});
+        size_t i = 0;
+        while (i < m.size()) {
+            Chunk c{p, {}, {}};
+            while (i < m.size() && c.agents.size() < (size_t)kMaxAgentsPerLaunch) {
+                const pkv_pool* q = private_of(m[i]);
+                const bool seen = !q || std::find(c.privs.begin(), c.privs.end(), q) != c.privs.end();
+                if (!seen && c.privs.size() + 1 >= (size_t)kMaxPoolsPerLaunch) break;
+                if (!seen) c.privs.push_back(q);
+                c.agents.push_back(m[i]);
+                ++i;
+            }
+            std::stable_sort(c.agents.begin(), c.agents.end(), [&](int u, int v) {
+                auto rank = [&](int a) {
+                    const pkv_pool* q = private_of(a);
+                    return q ? 1 + (int)(std::find(c.privs.begin(), c.privs.end(), q) - c.privs.begin()) : 0;
+                };
+                return rank(u) < rank(v);
+            });
+            chunks.push_back(std::move(c));
+        }
     }
     size_t ci = 0;
     while (ci < chunks.size()) {
@@ -853,11 +898,10 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
         L.sm_log2 = sigma * 1.4426950408889634f;
         int n_agents = 0, wg = 0;
         uint64_t part = 0;
-        while (ci < chunks.size() && L.n_pools < kMaxPoolsPerLaunch &&
-               n_agents + (int)chunks[ci].agents.size() <= kMaxAgentsPerLaunch) {
-            const Chunk& c = chunks[ci];
+        // one pool entry: rows are (agents[i], head of the group) for the launch agents
+        // agent0 .. agent0 + n - 1, which are call agents `agents`
+        auto add_pool = [&](const pkv_pool* p, int agent0, const std::vector<int>& agents) {
             PoolEntry& e = L.pools[L.n_pools];
-            const pkv_pool* p = c.pool;
             e.base = static_cast<const uint8_t*>(p->base);
             e.off_kq = p->off_kq;
             e.off_vn = p->off_vn;
@@ -870,8 +914,8 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             }
             e.T = p->n_tokens[x->layer_begin];
             e.tc = p->tc;
-            e.rows = (int)c.agents.size() * G;
-            e.agent0 = n_agents;
+            e.rows = (int)agents.size() * G;
+            e.agent0 = agent0;
             const int units = x->layer_count * hkv;
             const int tiles = std::max(1, (e.T + kTile - 1) / kTile);
             int splits = x->splits;
@@ -887,20 +931,45 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.part_off = part;
             part += (uint64_t)units * e.splits * e.rows * record_floats(d);
             wg += units * e.splits * e.rblocks;
-            e.agent_base = c.agents[0];
-            for (size_t i = 0; i < c.agents.size(); ++i)
-                if (c.agents[i] != c.agents[0] + (int)i) e.agent_base = -1;
+            e.agent_base = agents[0];
+            for (size_t i = 0; i < agents.size(); ++i)
+                if (agents[i] != agents[0] + (int)i) e.agent_base = -1;
+            return L.n_pools++;
+        };
+        while (ci < chunks.size() && L.n_pools + 1 + (int)chunks[ci].privs.size() <= kMaxPoolsPerLaunch &&
+               n_agents + (int)chunks[ci].agents.size() <= kMaxAgentsPerLaunch) {
+            const Chunk& c = chunks[ci];
+            const int shared = add_pool(c.pool, n_agents, c.agents);
             for (size_t i = 0; i < c.agents.size(); ++i) {
                 const int a = c.agents[i];
-                L.agent_id[n_agents] = (int16_t)a;
-                L.agent_pool[n_agents] = (int16_t)L.n_pools;
-                L.agent_pos[n_agents] = (int16_t)i;
-                const int s = x->sfx_len ? x->sfx_len[a] : 0;
-                L.sfx_len[n_agents] = s;
-                if (s > 0) L.has_sfx = 1;
-                ++n_agents;
+                const int k = n_agents + (int)i;
+                L.agent_id[k] = (int16_t)a;
+                L.agent_pool[k] = (int16_t)shared;
+                L.agent_pos[k] = (int16_t)i;
+                L.agent_pool2[k] = -1;
+                L.agent_pos2[k] = 0;
+                const int sl = x->sfx_len ? x->sfx_len[a] : 0;
+                L.sfx_len[k] = sl;
+                if (sl > 0) L.has_sfx = 1;
             }
-            ++L.n_pools;
+            // private pools: their agents are consecutive within the chunk
+            size_t i = 0;
+            while (i < c.agents.size()) {
+                const pkv_pool* q = private_of(c.agents[i]);
+                size_t j = i;
+                while (j < c.agents.size() && private_of(c.agents[j]) == q) ++j;
+                if (q) {
+                    const std::vector<int> grp(c.agents.begin() + i, c.agents.begin() + j);
+                    const int ent = add_pool(q, n_agents + (int)i, grp);
+                    for (size_t t = i; t < j; ++t) {
+                        L.agent_pool2[n_agents + t] = (int16_t)ent;
+                        L.agent_pos2[n_agents + t] = (int16_t)(t - i);
+                    }
+                    L.has_private = 1;
+                }
+                i = j;
+            }
+            n_agents += (int)c.agents.size();
             ++ci;
         }
         L.n_agents = n_agents;
@@ -941,6 +1010,24 @@ int validate(const pkv_decode_args* x) {
             if (p->n_tokens[l] != T) return PKV_EINVAL;
         if (T < 0 || T > p->cfg.capacity_tokens) return PKV_EINVAL;
     }
+    if (x->agent_private_pool) {
+        for (int a = 0; a < x->n_agents; ++a) {
+            const pkv_pool* p = x->agent_private_pool[a];
+            if (!p) continue;
+            if (!p->base) return PKV_EINVAL;
+            int err;
+            if (!config_valid(&p->cfg, &err)) return err;
+            if (p->cfg.n_kv_heads != p0->cfg.n_kv_heads || p->cfg.head_dim != p0->cfg.head_dim) return PKV_EINVAL;
+            if (x->layer_begin + x->layer_count > p->cfg.n_layers) return PKV_EINVAL;
+            const int T = p->n_tokens[x->layer_begin];
+            for (int l = x->layer_begin; l < x->layer_begin + x->layer_count; ++l)
+                if (p->n_tokens[l] != T) return PKV_EINVAL;
+            if (T < 0 || T > p->cfg.capacity_tokens) return PKV_EINVAL;
+            // a private pool is attended in addition to the shared one, never instead of it
+            for (int b = 0; b < x->n_agents; ++b)
+                if (x->agent_pool[b] == p) return PKV_EINVAL;
+        }
+    }
     if (x->n_q_heads % p0->cfg.n_kv_heads) return PKV_EINVAL;
     bool any_sfx = false;
     for (int a = 0; a < x->n_agents; ++a) {
@@ -978,7 +1065,7 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
             // one split per (pool, layer, kv head): the MFMA kernel finishes the rows itself
-            L.fused = 1;
+            L.fused = L.has_private ? 0 : 1;
             for (int p = 0; p < L.n_pools; ++p) L.fused &= L.pools[p].splits == 1;
             const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
             if (st != PKV_OK) return st;
@@ -1013,7 +1100,11 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
     int max_rows = 0;
     {
         std::map<const pkv_pool*, int> cnt;
-        for (int a = 0; a < args->n_agents; ++a) max_rows = std::max(max_rows, ++cnt[args->agent_pool[a]]);
+        for (int a = 0; a < args->n_agents; ++a) {
+            max_rows = std::max(max_rows, ++cnt[args->agent_pool[a]]);
+            const pkv_pool* q = args->agent_private_pool ? args->agent_private_pool[a] : nullptr;
+            if (q) max_rows = std::max(max_rows, ++cnt[q]);
+        }
         max_rows *= args->n_q_heads / args->agent_pool[0]->cfg.n_kv_heads;
     }
     // fp32 queries need hi + lo query operands; above 48 rows they do not fit the registers

@@ -439,14 +439,29 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     constexpr int QV = QSPLIT ? 2 : 1;
     uint4 qraw[RT][KS][QV];
     bool rok[RT];
+    // the rows' agents and heads first (a table lookup only when the pool's agents are not
+    // consecutive call agents), so that no wait for a lookup falls between the query loads
+    int q_agent[RT], q_head[RT];
+    const float rG = __builtin_amdgcn_rcpf((float)a.G);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = 16 * rt + rl;
         rok[rt] = rho < R;
         const int rr = rok[rt] ? rho : 0;
-        const int agent = P.agent_base >= 0 ? P.agent_base + rr / a.G : a.agent_id[P.agent0 + rr / a.G];
-        const int head = g * a.G + rr % a.G;
-        const uint64_t qo = (((uint64_t)agent * a.lc + lj) * a.hq + head) * D + lg * DL;
+        const int ka = (int)(((float)rr + 0.5f) * rG);  // rr / G, exact for rows < 2^20
+        q_agent[rt] = P.agent0 + ka;
+        q_head[rt] = g * a.G + rr - ka * a.G;
+    }
+    if (P.agent_base >= 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) q_agent[rt] += P.agent_base - P.agent0;
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) q_agent[rt] = a.agent_id[q_agent[rt]];
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint64_t qo = (((uint64_t)q_agent[rt] * a.lc + lj) * a.hq + q_head[rt]) * D + lg * DL;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             if constexpr (QSPLIT) {

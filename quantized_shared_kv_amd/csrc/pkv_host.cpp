@@ -156,7 +156,7 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 101; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {

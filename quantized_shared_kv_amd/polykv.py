@@ -14,6 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
+ABI_VERSION = 101  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -45,7 +46,7 @@ class DecodeArgs(ctypes.Structure):
                 ("agent_pool", POINTER(POINTER(Pool))), ("q", c_void_p), ("q_dtype", c_int32),
                 ("sfx_k", c_void_p), ("sfx_v", c_void_p), ("sfx_dtype", c_int32), ("sfx_cap", c_int32),
                 ("sfx_len", POINTER(c_int32)), ("out", c_void_p), ("kernel", c_int32), ("splits", c_int32),
-                ("pool_events", POINTER(c_void_p))]
+                ("pool_events", POINTER(c_void_p)), ("agent_private_pool", POINTER(POINTER(Pool)))]
 
 
 _LIB = None
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         for i, s in enumerate((PoolConfig, Pool, DecodeArgs)):
             if L.pkv_abi_sizeof(i) != ctypes.sizeof(s):
                 raise ImportError(f"ABI mismatch for {s.__name__}")
+        if L.pkv_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.pkv_version()}, this binding expects {ABI_VERSION}: rebuild it")
         _LIB = L
     return _LIB
 
@@ -137,7 +140,7 @@ def pool_quantize_append(pool: Pool, layer_begin: int, k, v, stream=None) -> Non
 
 
 def _decode_args(pools, q, out, layer_begin, sfx_k=None, sfx_v=None, sfx_len=None, softmax_scale=0.0,
-                 kernel=KERNEL_DEFAULT, splits=0, pool_events=None):
+                 kernel=KERNEL_DEFAULT, splits=0, pool_events=None, private_pools=None):
     n_agents = len(pools)
     arr = (POINTER(Pool) * max(n_agents, 1))(*[ctypes.pointer(p) for p in pools])
     lens = (c_int32 * max(n_agents, 1))(*(list(sfx_len) if sfx_len is not None else [0] * n_agents))
@@ -163,20 +166,30 @@ def _decode_args(pools, q, out, layer_begin, sfx_k=None, sfx_v=None, sfx_len=Non
     if pool_events is not None:
         evs = (c_void_p * 2)(*[e.cuda_event if hasattr(e, "cuda_event") else e for e in pool_events])
         a.pool_events = ctypes.cast(evs, POINTER(c_void_p))
-    return a, (arr, lens, evs)
+    prv = None
+    if private_pools is not None:
+        if len(private_pools) != n_agents:
+            raise ValueError("private_pools needs one entry (a Pool or None) per agent")
+        prv = (POINTER(Pool) * max(n_agents, 1))(*[ctypes.pointer(p) if p is not None else None
+                                                   for p in private_pools])
+        a.agent_private_pool = prv
+    return a, (arr, lens, evs, prv)
 
 
 def agent_decode_attention(pools, q, out, layer_begin=0, sfx_k=None, sfx_v=None, sfx_len=None, workspace=None,
                            softmax_scale=0.0, kernel=KERNEL_DEFAULT, splits=0, stream=None,
-                           pool_events=None) -> int:
+                           pool_events=None, private_pools=None) -> int:
     """Enqueue one decode call.  pools: list of Pool (one per agent; the same object = shared pool).
+
+    private_pools: optional list with one entry per agent, a Pool the agent also attends
+    (its own older tokens, quantized once) or None.
 
     With workspace=None only the required workspace size is computed and returned.
     pool_events: optional pair of recorded torch.cuda.Event (or raw hipEvent_t handles)
     bracketing the pool kernel.  Returns the workspace bytes the call needs.
     """
     a, keep = _decode_args(pools, q, out, layer_begin, sfx_k, sfx_v, sfx_len, softmax_scale, kernel, splits,
-                           pool_events)
+                           pool_events, private_pools)
     size = c_size_t(0)
     if workspace is None:
         _check(lib().agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None), "agent_decode_attention")

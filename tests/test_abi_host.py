@@ -39,7 +39,7 @@ def test_struct_mirrors_match_c_sizes():
     assert lib.pkv_abi_sizeof(1) == ctypes.sizeof(pk.Pool)
     assert lib.pkv_abi_sizeof(2) == ctypes.sizeof(pk.DecodeArgs)
     assert lib.pkv_abi_sizeof(3) == 0
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == pk.ABI_VERSION
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 64, 512, [3]), (24, 32, 64, 1851, [3] * 24), (32, 8, 128, 4096, [3] * 32),
@@ -195,3 +195,34 @@ def test_decode_workspace_query_and_errors():
     a.n_agents = 0
     assert lib.agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None) == 0 and size.value == 0
     del keep
+
+
+def test_decode_private_pools_workspace_and_errors():
+    """Private pools add their partial records to the workspace; they must match the shared
+    pools' heads and head_dim, hold the call's layers uniformly, and not be a shared pool."""
+    pool = _fake_pool(L=2, H=2, d=64, cap=100)
+    pool.n_tokens[0] = pool.n_tokens[1] = 70
+    A, lc, hq, d = 3, 2, 4, 64
+    q = _FakeT((A, lc, hq, d), 1 << 24)
+    out = _FakeT((A, lc, hq, d), 1 << 25, "f32")
+    base = pk.agent_decode_attention([pool] * A, q, out)
+    prv = _fake_pool(L=2, H=2, d=64, cap=40)
+    prv.n_tokens[0] = prv.n_tokens[1] = 40
+    ws = pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv, None, None])
+    G = hq // 2
+    assert ws >= base + lc * 2 * 1 * G * (2 + d) * 4  # at least one split of the private pool's rows
+    assert pk.agent_decode_attention([pool] * A, q, out, private_pools=[None] * A) == base
+    empty = _fake_pool(L=2, H=2, d=64, cap=8)  # a private pool with no tokens is allowed
+    pk.agent_decode_attention([pool] * A, q, out, private_pools=[empty, prv, None])
+    with pytest.raises(pk.PolyKVError):  # head_dim differs from the shared pool's
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[_fake_pool(L=2, H=2, d=128, cap=8), None, None])
+    with pytest.raises(pk.PolyKVError):  # fewer layers than the call
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[_fake_pool(L=1, H=2, d=64, cap=8), None, None])
+    prv.n_tokens[1] = 39
+    with pytest.raises(pk.PolyKVError):  # unequal token counts across the call's layers
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv, None, None])
+    prv.n_tokens[1] = 40
+    with pytest.raises(pk.PolyKVError):  # a shared pool named as a private one
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[pool, None, None])
+    with pytest.raises(ValueError):  # one entry per agent
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv])

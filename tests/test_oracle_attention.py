@@ -132,3 +132,38 @@ def test_max_rel_error_definition():
     ref = np.array([[1.0, -2.0, 0.5], [0.0, 0.0, 0.0]])
     out = ref + np.array([[0.002, 0.0, 0.0], [1e-7, 0.0, 0.0]])
     assert attention.max_rel_error(out, ref) == pytest.approx(max(0.002 / 2.0, 1e-7 / 1e-6))
+
+
+def test_private_segment_equals_a_second_append_block():
+    """A pool appended in two blocks decodes to the same K/V (K scales are per block, V codes per
+    token) as a pool of the first block plus a private segment of the second, so attending to
+    pool + private segment must give exactly what attending to the two-block pool gives."""
+    rng = np.random.default_rng(7)
+    H, d, Hq = 2, 64, 4
+    k1, v1 = rng.standard_normal((1, H, 40, d)).astype(np.float32), rng.standard_normal((1, H, 40, d)).astype(np.float32)
+    k2 = (3 * rng.standard_normal((1, H, 24, d))).astype(np.float32)
+    v2 = (0.5 * rng.standard_normal((1, H, 24, d))).astype(np.float32)
+    whole = pool_image.PoolImage(1, H, d, 64, [3])
+    whole.append(0, k1, v1)
+    whole.append(0, k2, v2)
+    first = pool_image.PoolImage(1, H, d, 40, [3])
+    first.append(0, k1, v1)
+    second = pool_image.PoolImage(1, H, d, 24, [3])
+    second.append(0, k2, v2)
+    q = rng.standard_normal((2, 1, Hq, d))
+    ks = rng.standard_normal((2, 1, H, 5, d))
+    vs = rng.standard_normal((2, 1, H, 5, d))
+    ref = attention.decode_call(q, [0, 0], lambda p, l, g: whole.decoded_layer(l, g), lambda a, l: ks[a, l],
+                                lambda a, l: vs[a, l], [5, 3], H)
+    out = attention.decode_call(q, [0, 0], lambda p, l, g: first.decoded_layer(l, g), lambda a, l: ks[a, l],
+                                lambda a, l: vs[a, l], [5, 3], H,
+                                private=lambda a, l, g: second.decoded_layer(l, g))
+    assert np.array_equal(out, ref)
+    # an agent without a private segment (None) is unaffected by the others having one
+    mixed = attention.decode_call(q, [0, 0], lambda p, l, g: first.decoded_layer(l, g), lambda a, l: ks[a, l],
+                                  lambda a, l: vs[a, l], [5, 3], H,
+                                  private=lambda a, l, g: second.decoded_layer(l, g) if a == 0 else None)
+    plain = attention.decode_call(q, [0, 0], lambda p, l, g: first.decoded_layer(l, g), lambda a, l: ks[a, l],
+                                  lambda a, l: vs[a, l], [5, 3], H)
+    assert np.array_equal(mixed[0], ref[0]) and np.array_equal(mixed[1], plain[1])
+    assert not np.allclose(plain[0], ref[0])  # the segment does change the output
