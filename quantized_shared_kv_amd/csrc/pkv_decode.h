@@ -25,6 +25,8 @@ struct PoolEntry {
     int32_t chunk;         // tokens per split (multiple of 32)
     int32_t rblocks;       // row blocks per (layer, kv head, split)
     int32_t wg_begin;      // first workgroup of this pool in the launch
+    int32_t seg_begin;     // >= 0: a private segment decoded by k_seg (no pool-kernel workgroups),
+                           // its first unit there; -1: decoded by the pool kernel
     int32_t agent_base;    // >= 0: the pool's launch agents agent0 + i are call agents
                            // agent_base + i (no table lookup needed); -1 otherwise
 };
@@ -51,6 +53,7 @@ struct DecodeLaunch {
     int32_t has_sfx;
     int32_t fused;          // the pool kernel finishes the outputs itself (one split everywhere)
     int32_t has_private;    // some agent also attends a private pool (outputs merged by k_merge)
+    int32_t seg_units;      // k_seg units: (agent, layer, kv head) of the small private pools
     float sm_log2;          // softmax scale * log2(e)
 };
 

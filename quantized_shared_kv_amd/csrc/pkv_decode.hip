@@ -720,6 +720,284 @@ __global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
     sfx_fast_wave<D, RS>(a, unit, sbuf[wave]);
 }
 
+// ------------------------------------------------------------------ private segments
+// A private segment (a pool of at most 8 rows: one agent's own older tokens) is decoded
+// by one wavefront per (segment agent, layer, kv head), like the native suffix, with
+// the pool's encoding: scores from int8 K as exact fp16 (1152 + k, the offset removed
+// by starting each lane's sum at -1152 * its query values) against fp16 query pairs
+// (v_dot2_f32_f16); V accumulated in the rotated domain, acc = sum p * Vn * c[code],
+// from an fp32 centroid table in LDS.  The result is a partial record (m, l, acc) in
+// the pool kernels' layout (one split), merged by k_merge with the shared pool's.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_h2f(float lo, float hi) {
+    const half2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 4 int8 codes -> 4 fp16 values 1152 + k (offset byte in the mantissa of 1024), as two pairs
+__device__ __forceinline__ void i8x4_to_h2x2(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = w ^ 0x80808080u;
+    lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+}
+
+template <int D, int RS, int BITS>
+__device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int jpos, int lj, int g, float* sbuf,
+                         const float* cent) {
+    // score sweep: LPT lanes per token, 16 dimensions (16 bytes of K) each
+    constexpr int LPT = D / 16;
+    constexpr int TPP = 64 / LPT;                  // tokens per load instruction
+    constexpr int KG = 32;                         // tokens per score group
+    constexpr int KU = KG / TPP;
+    constexpr int RPL = RS / LPT > 1 ? RS / LPT : 1;
+    constexpr int LB = LPT == 4 ? 2 : 3;           // log2 LPT
+    constexpr int LS = RS / RPL == 1 ? 0 : RS / RPL == 2 ? 1 : RS / RPL == 4 ? 2 : 3;
+    // value sweep: 4 dimensions per lane, LVG lanes per 8-token group, GP groups at once
+    constexpr int LVG = D / 4;
+    constexpr int GP = 64 / LVG;
+    constexpr int FW = BITS;                       // field dwords of 4 dimensions (4 * 8 * BITS bits)
+    static_assert((1 << LS) * RPL == RS && (GP == 2 || GP == 4), "segment tiling");
+
+    const int lane = threadIdx.x & 63;
+    const int l = a.l0 + lj;
+    const int T = P.T;
+    const int agent = P.agent_base >= 0 ? P.agent_base + jpos : a.agent_id[P.agent0 + jpos];
+    const int8_t* kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
+    const float* vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
+    const float* ks = reinterpret_cast<const float*>(P.base + P.off_ks) + (uint64_t)l * P.tc;
+    const uint8_t* vc = P.base + P.off_vc0 + (uint64_t)a.hkv * P.tc * (D / 8) * layer_bits_prefix(P, l) +
+                        (uint64_t)g * (P.tc / 8) * D * BITS;
+    const int part = lane % LPT, tl = lane / LPT;
+    int rb = 0;
+    if constexpr (LS >= 1) rb += (lane & 1) * (RS / 2);
+    if constexpr (LS >= 2) rb += ((lane >> 1) & 1) * (RS / 4);
+    if constexpr (LS >= 3) rb += ((lane >> 2) & 1) * (RS / 8);
+    const bool swriter = ((lane & (LPT - 1)) >> LS) == 0;
+    const int gs = lane / LVG, db = lane % LVG;  // value sweep: group slot, dimension block
+
+    for (int r0 = 0; r0 < a.G; r0 += RS) {
+        const int nr = min(RS, a.G - r0);
+        // query slices as fp16 pairs (dims 16 part .. 16 part + 15) and the offset start
+        uint32_t qp[RS][8];
+        float qoff[RS];
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+            const int rr = min(r0 + r, a.G - 1);
+            const uint64_t qo = (((uint64_t)agent * a.lc + lj) * a.hq + g * a.G + rr) * D + 16 * part;
+            float x[16];
+            if (a.q_dtype == PKV_BF16) {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo);
+                const uint4 w0 = src[0], w1 = src[1];
+                const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[2 * i] = __uint_as_float(w[i] << 16);
+                    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x[i] = static_cast<const float*>(a.q)[qo + i];
+            }
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qp[r][i] = pack_h2f(x[2 * i], x[2 * i + 1]);
+                const half2_t h = __builtin_bit_cast(half2_t, qp[r][i]);
+                sum += (float)h[0] + (float)h[1];
+            }
+            qoff[r] = -1152.0f * sum;
+        }
+        float M[RS], Lp[RS], acc[RS][4];
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+            M[r] = -INFINITY;
+            Lp[r] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
+        }
+        for (int c0 = 0; c0 < T; c0 += kSfxChunk) {
+            const int nc = min(kSfxChunk, T - c0);
+            // ---- scores (log2 units) into sbuf[t][r]
+            float mloc[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) mloc[i] = -INFINITY;
+            for (int g0 = 0; g0 < nc; g0 += KG) {
+                uint4 kk[KU];
+#pragma unroll
+                for (int u = 0; u < KU; ++u) {
+                    const int t = min(g0 + u * TPP + tl, nc - 1);
+                    kk[u] = *reinterpret_cast<const uint4*>(kq + (uint64_t)(c0 + t) * D + 16 * part);
+                }
+#pragma unroll
+                for (int u = 0; u < KU; ++u) {
+                    const int t = g0 + u * TPP + tl;
+                    const bool ok = t < nc;
+                    uint32_t kh[8];
+                    i8x4_to_h2x2(kk[u].x, kh[0], kh[1]);
+                    i8x4_to_h2x2(kk[u].y, kh[2], kh[3]);
+                    i8x4_to_h2x2(kk[u].z, kh[4], kh[5]);
+                    i8x4_to_h2x2(kk[u].w, kh[6], kh[7]);
+                    float sc[RS];
+#pragma unroll
+                    for (int r = 0; r < RS; ++r) {
+                        sc[r] = qoff[r];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            sc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kh[i]),
+                                                           __builtin_bit_cast(half2_t, qp[r][i]), sc[r], false);
+                    }
+                    auto red = [&](auto bt) {
+                        constexpr int b = decltype(bt)::value;
+                        if constexpr (b < LS) scatter_add<(1 << b), (RS >> b)>(sc, lane & (1 << b));
+                        else if constexpr (b < LB) all_add<(1 << b), RPL>(sc);
+                    };
+                    red(std::integral_constant<int, 0>{});
+                    red(std::integral_constant<int, 1>{});
+                    red(std::integral_constant<int, 2>{});
+                    const float f = ks[c0 + min(t, nc - 1)] * a.sm_log2;
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        const float x = sc[i] * f;
+                        if (ok) {
+                            mloc[i] = fmaxf(mloc[i], x);
+                            if (swriter) sbuf[t * RS + rb + i] = x;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+#pragma unroll
+                for (int off = LPT; off < 64; off <<= 1) mloc[i] = fmaxf(mloc[i], __shfl_xor(mloc[i], off, 64));
+            }
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                const int qq = r / RPL;
+                int src = 0;
+#pragma unroll
+                for (int b = 0; b < LS; ++b) src |= ((qq >> (LS - 1 - b)) & 1) << b;
+                const float mc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mloc[r % RPL]), src));
+                const float mn = fmaxf(M[r], mc);
+                const float alpha = (M[r] == -INFINITY) ? 0.0f : exp2f(M[r] - mn);
+                M[r] = mn;
+                Lp[r] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r][e] *= alpha;
+            }
+            __builtin_amdgcn_wave_barrier();
+            // ---- probabilities: l sums p, the value sweep uses w = p * Vn; tokens past the
+            // chunk (to the end of its last 8-token group) get w = 0
+            for (int t = lane; t < ((nc + 7) & ~7); t += 64) {
+                const float n = t < nc ? vn[c0 + t] : 0.0f;
+#pragma unroll
+                for (int r = 0; r < RS; ++r) {
+                    const float p = t < nc ? exp2f(sbuf[t * RS + r] - M[r]) : 0.0f;
+                    Lp[r] += p;
+                    sbuf[t * RS + r] = p * n;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            // ---- values: 8-token groups, 4 dimensions per lane, GP groups side by side
+            const int ng = (nc + 7) / 8;
+            for (int gi = gs; gi < ng; gi += GP) {
+                const uint32_t* fp = reinterpret_cast<const uint32_t*>(vc + (uint64_t)((c0 >> 3) + gi) * (D * BITS)) +
+                                     FW * db;
+                uint32_t fw[FW];
+#pragma unroll
+                for (int i = 0; i < FW; ++i) fw[i] = fp[i];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int t = 8 * gi + i;
+                    float w[RS];
+                    if constexpr (RS >= 4) {
+#pragma unroll
+                        for (int r4 = 0; r4 < RS; r4 += 4) {
+                            const float4 w4 = *reinterpret_cast<const float4*>(&sbuf[t * RS + r4]);
+                            w[r4] = w4.x;
+                            w[r4 + 1] = w4.y;
+                            w[r4 + 2] = w4.z;
+                            w[r4 + 3] = w4.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < RS; ++r) w[r] = sbuf[t * RS + r];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // dimension 4 db + e: bits [8 BITS e + BITS i, +BITS) of the 4 fields
+                        const int bit = 8 * BITS * e + BITS * i;
+                        const uint32_t lo = fw[bit >> 5] >> (bit & 31);
+                        const uint32_t code = ((bit & 31) + BITS > 32 ? (lo | (fw[(bit >> 5) + 1] << (32 - (bit & 31))))
+                                                                      : lo) & ((1u << BITS) - 1u);
+                        const float c = cent[code];
+#pragma unroll
+                        for (int r = 0; r < RS; ++r) acc[r][e] = fmaf(w[r], c, acc[r][e]);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        // ---- records: l over all lanes; acc over the group slots
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) Lp[r] += __shfl_xor(Lp[r], off, 64);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[r][e] += __shfl_xor(acc[r][e], LVG, 64);
+                if constexpr (GP == 4) acc[r][e] += __shfl_xor(acc[r][e], 2 * LVG, 64);
+            }
+        }
+        const int rho0 = jpos * a.G + r0;
+        float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.rows) * (2 + D);
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+            if (r >= nr) break;
+            float* rec = rec0 + (uint64_t)(rho0 + r) * (2 + D);
+            if (gs == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rec[2 + 4 * db + e] = acc[r][e];
+            }
+            if (lane == 0) {
+                rec[0] = T > 0 ? M[r] : -INFINITY;
+                rec[1] = Lp[r];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// grid: ceil(segment units / 4), 256 threads; a unit is (segment pool, its agent, layer, kv head)
+template <int D, int RS>
+__global__ void __launch_bounds__(256) k_seg(DecodeLaunch a, Centroids cents) {
+    __shared__ __align__(16) float sbuf[4][kSfxChunk * RS];
+    __shared__ float cent[3][16];
+    if (threadIdx.x < 48) cent[threadIdx.x / 16][threadIdx.x % 16] = cents.c[threadIdx.x / 16][threadIdx.x % 16];
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int unit = blockIdx.x * 4 + wave;
+    int p = -1;
+    for (int i = 0; i < a.n_pools; ++i) {
+        const PoolEntry& e = a.pools[i];
+        if (e.seg_begin < 0) continue;
+        const int n = (e.rows / a.G) * a.lc * a.hkv;
+        if (unit >= e.seg_begin && unit < e.seg_begin + n) p = i;
+    }
+    if (p < 0) return;
+    const PoolEntry& P = a.pools[p];
+    unit -= P.seg_begin;
+    const int g = unit % a.hkv;
+    const int lj = (unit / a.hkv) % a.lc;
+    const int jpos = unit / (a.hkv * a.lc);
+    const int l = a.l0 + lj;
+    switch (layer_bits(P, l)) {
+        case 2: seg_wave<D, RS, 2>(a, P, P.agent0 + jpos, jpos, lj, g, sbuf[wave], cent[0]); break;
+        case 3: seg_wave<D, RS, 3>(a, P, P.agent0 + jpos, jpos, lj, g, sbuf[wave], cent[1]); break;
+        default: seg_wave<D, RS, 4>(a, P, P.agent0 + jpos, jpos, lj, g, sbuf[wave], cent[2]); break;
+    }
+}
+
 // grid ceil(n_agents * lc * hkv / 4), 256 threads = 4 wavefronts, one unit each
 template <int D>
 __global__ void __launch_bounds__(256) k_sfx(DecodeLaunch a) {
@@ -900,7 +1178,8 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
         uint64_t part = 0;
         // one pool entry: rows are (agents[i], head of the group) for the launch agents
         // agent0 .. agent0 + n - 1, which are call agents `agents`
-        auto add_pool = [&](const pkv_pool* p, int agent0, const std::vector<int>& agents) {
+        // seg: a private segment of at most 8 rows, decoded by k_seg instead of the pool kernel
+        auto add_pool = [&](const pkv_pool* p, int agent0, const std::vector<int>& agents, bool seg = false) {
             PoolEntry& e = L.pools[L.n_pools];
             e.base = static_cast<const uint8_t*>(p->base);
             e.off_kq = p->off_kq;
@@ -928,9 +1207,17 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.splits = std::max(1, (std::max(e.T, 1) + e.chunk - 1) / e.chunk);
             e.rblocks = use_mfma ? 1 : (e.rows + kValuRows - 1) / kValuRows;
             e.wg_begin = wg;
+            e.seg_begin = -1;
+            if (seg) {
+                e.splits = 1;
+                e.chunk = std::max(e.T, 1);
+                e.rblocks = 1;
+                e.seg_begin = L.seg_units;
+                L.seg_units += (int)agents.size() * units;
+            }
             e.part_off = part;
             part += (uint64_t)units * e.splits * e.rows * record_floats(d);
-            wg += units * e.splits * e.rblocks;
+            if (!seg) wg += units * e.splits * e.rblocks;
             e.agent_base = agents[0];
             for (size_t i = 0; i < agents.size(); ++i)
                 if (agents[i] != agents[0] + (int)i) e.agent_base = -1;
@@ -960,7 +1247,8 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
                 while (j < c.agents.size() && private_of(c.agents[j]) == q) ++j;
                 if (q) {
                     const std::vector<int> grp(c.agents.begin() + i, c.agents.begin() + j);
-                    const int ent = add_pool(q, n_agents + (int)i, grp);
+                    const bool seg = x->q_dtype == PKV_BF16 && (int)grp.size() * G <= 8;
+                    const int ent = add_pool(q, n_agents + (int)i, grp, seg);
                     for (size_t t = i; t < j; ++t) {
                         L.agent_pool2[n_agents + t] = (int16_t)ent;
                         L.agent_pos2[n_agents + t] = (int16_t)(t - i);
@@ -1061,6 +1349,13 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
             } else {
                 hipLaunchKernelGGL(k_sfx<D>, grid, dim3(kThreads), 0, s, L);
             }
+        }
+        if (L.seg_units > 0) {
+            const dim3 grid((L.seg_units + 3) / 4);
+            if (L.G == 1) hipLaunchKernelGGL((k_seg<D, 1>), grid, dim3(kThreads), 0, s, L, cents);
+            else if (L.G == 2) hipLaunchKernelGGL((k_seg<D, 2>), grid, dim3(kThreads), 0, s, L, cents);
+            else if (L.G <= 4) hipLaunchKernelGGL((k_seg<D, 4>), grid, dim3(kThreads), 0, s, L, cents);
+            else hipLaunchKernelGGL((k_seg<D, 8>), grid, dim3(kThreads), 0, s, L, cents);
         }
         if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
