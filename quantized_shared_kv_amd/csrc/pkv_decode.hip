@@ -748,7 +748,7 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
     // score sweep: LPT lanes per token, 16 dimensions (16 bytes of K) each
     constexpr int LPT = D / 16;
     constexpr int TPP = 64 / LPT;                  // tokens per load instruction
-    constexpr int KG = 32;                         // tokens per score group
+    constexpr int KG = RS >= 8 ? 32 : 64;          // tokens per score group
     constexpr int KU = KG / TPP;
     constexpr int RPL = RS / LPT > 1 ? RS / LPT : 1;
     constexpr int LB = LPT == 4 ? 2 : 3;           // log2 LPT
@@ -757,6 +757,7 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
     constexpr int LVG = D / 4;
     constexpr int GP = 64 / LVG;
     constexpr int FW = BITS;                       // field dwords of 4 dimensions (4 * 8 * BITS bits)
+    constexpr int NGL = kSfxChunk / 8 / GP;        // 8-token groups per lane per chunk (value sweep)
     static_assert((1 << LS) * RPL == RS && (GP == 2 || GP == 4), "segment tiling");
 
     const int lane = threadIdx.x & 63;
@@ -818,6 +819,18 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
         }
         for (int c0 = 0; c0 < T; c0 += kSfxChunk) {
             const int nc = min(kSfxChunk, T - c0);
+            const int ng = (nc + 7) / 8;
+            // this lane's code fields of the chunk's groups gs, gs + GP, ..., loaded now so that
+            // they arrive while the scores are computed
+            uint32_t fw[NGL][FW];
+#pragma unroll
+            for (int q = 0; q < NGL; ++q) {
+                const int gi = min(gs + q * GP, ng - 1);  // past the chunk: a valid group, not used
+                const uint32_t* fp =
+                    reinterpret_cast<const uint32_t*>(vc + (uint64_t)((c0 >> 3) + gi) * (D * BITS)) + FW * db;
+#pragma unroll
+                for (int i = 0; i < FW; ++i) fw[q][i] = fp[i];
+            }
             // ---- scores (log2 units) into sbuf[t][r]
             float mloc[RPL];
 #pragma unroll
@@ -899,13 +912,10 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
             }
             __builtin_amdgcn_wave_barrier();
             // ---- values: 8-token groups, 4 dimensions per lane, GP groups side by side
-            const int ng = (nc + 7) / 8;
-            for (int gi = gs; gi < ng; gi += GP) {
-                const uint32_t* fp = reinterpret_cast<const uint32_t*>(vc + (uint64_t)((c0 >> 3) + gi) * (D * BITS)) +
-                                     FW * db;
-                uint32_t fw[FW];
 #pragma unroll
-                for (int i = 0; i < FW; ++i) fw[i] = fp[i];
+            for (int q = 0; q < NGL; ++q) {
+                const int gi = gs + q * GP;
+                if (gi >= ng) break;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int t = 8 * gi + i;
@@ -927,9 +937,10 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
                     for (int e = 0; e < 4; ++e) {
                         // dimension 4 db + e: bits [8 BITS e + BITS i, +BITS) of the 4 fields
                         const int bit = 8 * BITS * e + BITS * i;
-                        const uint32_t lo = fw[bit >> 5] >> (bit & 31);
-                        const uint32_t code = ((bit & 31) + BITS > 32 ? (lo | (fw[(bit >> 5) + 1] << (32 - (bit & 31))))
-                                                                      : lo) & ((1u << BITS) - 1u);
+                        const uint32_t lo = fw[q][bit >> 5] >> (bit & 31);
+                        const uint32_t code =
+                            ((bit & 31) + BITS > 32 ? (lo | (fw[q][(bit >> 5) + 1] << (32 - (bit & 31)))) : lo) &
+                            ((1u << BITS) - 1u);
                         const float c = cent[code];
 #pragma unroll
                         for (int r = 0; r < RS; ++r) acc[r][e] = fmaf(w[r], c, acc[r][e]);
@@ -1360,8 +1371,12 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
             // one split per (pool, layer, kv head): the MFMA kernel finishes the rows itself
-            L.fused = L.has_private ? 0 : 1;
+            // one split per (pool, layer, kv head) and every private pool a segment (its records
+            // written by k_seg above): the MFMA kernel finishes the rows itself
+            L.fused = 1;
             for (int p = 0; p < L.n_pools; ++p) L.fused &= L.pools[p].splits == 1;
+            for (int k = 0; k < L.n_agents; ++k)
+                if (L.agent_pool2[k] >= 0 && L.pools[L.agent_pool2[k]].seg_begin < 0) L.fused = 0;
             const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
             if (st != PKV_OK) return st;
         } else {

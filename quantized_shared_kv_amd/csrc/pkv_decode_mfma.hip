@@ -783,6 +783,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // now, so their latency overlaps the combine
     const int fq = lane >> 4, fl = lane & 15;
     float su_m[FI], su_l[FI], su_v[FI][FD];
+    float se_m[FI], se_l[FI], se_v[FI][FD];  // the agent's private segment record (rotated domain), if any
     int f_row[FI], f_head[FI], f_agent[FI];
     if (fused) {
         const float rG = __builtin_amdgcn_rcpf((float)a.G);
@@ -804,6 +805,21 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 su_l[i] = ru[1];
 #pragma unroll
                 for (int e = 0; e < FD; ++e) su_v[i][e] = ru[2 + FD * fl + e];
+            }
+            se_m[i] = -INFINITY;
+            se_l[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < FD; ++e) se_v[i][e] = 0.0f;
+            const int e2 = a.has_private ? a.agent_pool2[P.agent0 + ka] : -1;
+            if (e2 >= 0) {  // written by the segment kernel before this launch
+                const PoolEntry& Q = a.pools[e2];
+                const float* rs = a.part + Q.part_off +
+                                  (((uint64_t)lj * a.hkv + g) * Q.rows + a.agent_pos2[P.agent0 + ka] * a.G +
+                                   (f_head[i] - g * a.G)) * (2 + D);
+                se_m[i] = rs[0];
+                se_l[i] = rs[1];
+#pragma unroll
+                for (int e = 0; e < FD; ++e) se_v[i][e] = rs[2 + FD * fl + e];
             }
         }
     }
@@ -886,6 +902,19 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 z[e4 + 3] = fmaf(al[w], v.w, z[e4 + 3]);
             }
         }
+        // the private segment's rotated-domain record joins before the transform (z loses its
+        // weight scale nu here; M and L become those of pool + segment)
+        {
+            const float ms = se_m[i];
+            const float M1 = fmaxf(M, ms);
+            const float ap = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - M1);
+            const float as = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M1);
+            const float zs = ap * inv_nu;
+#pragma unroll
+            for (int e = 0; e < FD; ++e) z[e] = fmaf(z[e], zs, as * se_v[i][e]);
+            L = ap * L + as * se_l[i];
+            M = M1;
+        }
 #pragma unroll
         for (int h = 1; h < FD; h <<= 1)
 #pragma unroll
@@ -911,7 +940,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         const float au = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M2);
         const float denom = ap * L + au * su_l[i];
         const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
-        const float sp_ = ap * inv_nu * (1.0f / D) * rinv;
+        const float sp_ = ap * (1.0f / D) * rinv;
         const float su_ = au * rinv;
         float o[FD];
 #pragma unroll
