@@ -904,7 +904,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
         // the private segment's rotated-domain record joins before the transform (z loses its
         // weight scale nu here; M and L become those of pool + segment)
-        {
+        float zscale = inv_nu;  // weight scale still on z
+        if (a.has_private) {
             const float ms = se_m[i];
             const float M1 = fmaxf(M, ms);
             const float ap = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - M1);
@@ -914,6 +915,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             for (int e = 0; e < FD; ++e) z[e] = fmaf(z[e], zs, as * se_v[i][e]);
             L = ap * L + as * se_l[i];
             M = M1;
+            zscale = 1.0f;
         }
 #pragma unroll
         for (int h = 1; h < FD; h <<= 1)
@@ -940,7 +942,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         const float au = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M2);
         const float denom = ap * L + au * su_l[i];
         const float rinv = denom > 0.0f ? 1.0f / denom : 0.0f;
-        const float sp_ = ap * (1.0f / D) * rinv;
+        const float sp_ = ap * zscale * (1.0f / D) * rinv;
         const float su_ = au * rinv;
         float o[FD];
 #pragma unroll
