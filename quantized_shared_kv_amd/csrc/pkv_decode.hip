@@ -729,6 +729,7 @@ __global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
 // from an fp32 centroid table in LDS.  The result is a partial record (m, l, acc) in
 // the pool kernels' layout (one split), merged by k_merge with the shared pool's.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+constexpr int kSegChunk = 128;  // tokens per segment chunk (bounds the code fields held ahead)
 
 __device__ __forceinline__ uint32_t pack_h2f(float lo, float hi) {
     const half2_t v = {(_Float16)lo, (_Float16)hi};
@@ -757,7 +758,7 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
     constexpr int LVG = D / 4;
     constexpr int GP = 64 / LVG;
     constexpr int FW = BITS;                       // field dwords of 4 dimensions (4 * 8 * BITS bits)
-    constexpr int NGL = kSfxChunk / 8 / GP;        // 8-token groups per lane per chunk (value sweep)
+    constexpr int NGL = kSegChunk / 8 / GP;        // 8-token groups per lane per chunk (value sweep)
     static_assert((1 << LS) * RPL == RS && (GP == 2 || GP == 4), "segment tiling");
 
     const int lane = threadIdx.x & 63;
@@ -817,8 +818,8 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
         }
-        for (int c0 = 0; c0 < T; c0 += kSfxChunk) {
-            const int nc = min(kSfxChunk, T - c0);
+        for (int c0 = 0; c0 < T; c0 += kSegChunk) {
+            const int nc = min(kSegChunk, T - c0);
             const int ng = (nc + 7) / 8;
             // this lane's code fields of the chunk's groups gs, gs + GP, ..., loaded now so that
             // they arrive while the scores are computed
@@ -982,7 +983,7 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
 // grid: ceil(segment units / 4), 256 threads; a unit is (segment pool, its agent, layer, kv head)
 template <int D, int RS>
 __global__ void __launch_bounds__(256) k_seg(DecodeLaunch a, Centroids cents) {
-    __shared__ __align__(16) float sbuf[4][kSfxChunk * RS];
+    __shared__ __align__(16) float sbuf[4][kSegChunk * RS];
     __shared__ float cent[3][16];
     if (threadIdx.x < 48) cent[threadIdx.x / 16][threadIdx.x % 16] = cents.c[threadIdx.x / 16][threadIdx.x % 16];
     __syncthreads();
