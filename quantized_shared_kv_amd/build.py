@@ -3,7 +3,8 @@
     python -m quantized_shared_kv_amd.build
 
 The library is written to quantized_shared_kv_amd/_lib/libpolykv.so.  Every
-HIP translation unit is compiled with packed-fp32 instructions disabled.
+HIP translation unit is compiled with packed-fp32 instructions disabled, and
+matrix-core instructions write VGPRs (-amdgpu-mfma-vgpr-form).
 """
 from __future__ import annotations
 
@@ -33,6 +34,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # matrix-core results in VGPRs: the score tiles are read by vector instructions, so
+           # accumulating them in AGPRs cost a copy per value (the query operands sit in AGPRs)
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]

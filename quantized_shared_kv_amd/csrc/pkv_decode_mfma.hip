@@ -519,6 +519,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 }
             }
             qreg[rt][k] = hv.h;
+            asm volatile("" : "+a"(qreg[rt][k]));  // a matrix-core operand only: kept in AGPRs
             if constexpr (QSPLIT) qlo[rt][k] = lv.h;
         }
         // -1152 * sum of the row's fp16 query values: cancels the offset carried by K
