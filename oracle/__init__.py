@@ -17,6 +17,9 @@ Sources (the PolyKV and CoMixKV web pages; citations name page and section):
 * CoMixKV news article, "incremental quantization strategy": per-(agent, layer)
   2 to 4 bit widths; recent tokens stay at native precision; quantised blocks
   are never re-quantised.
+* CoMixKV news article, abstract and method: online sensitivity from recent
+  Q/K/V as a local attention-error bound; joint bit allocation over agents and
+  layers under a shared byte budget.
 
 Modules:
 
@@ -25,7 +28,9 @@ Modules:
 * ``codec``      K int8 codec, V rotate/normalise/code codec, code-group packing.
 * ``pool_image`` byte layout of one pool and a builder that writes it.
 * ``attention``  fp64 decode attention over decoded pool + native suffix.
+* ``comixkv``    CoMixKV controller: local attention-error sensitivity per
+  (agent, layer) and greedy joint 2/3/4-bit allocation under a byte budget.
 
 Readings of what the pages leave open are stated in each function's docstring.
 """
-from . import hadamard, lloyd_max, codec, pool_image, attention  # noqa: F401
+from . import hadamard, lloyd_max, codec, pool_image, attention, comixkv  # noqa: F401
