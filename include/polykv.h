@@ -196,6 +196,63 @@ typedef struct {
 int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
                            void* stream);
 
+/* ---- CoMixKV controller: sensitivity and joint bit allocation ---- */
+
+/* Arguments of one sensitivity estimate (CoMixKV news article, abstract and
+ * method: per-(agent, layer) sensitivity from the recently seen queries, keys
+ * and values, as a local attention-error bound, without calibration data or
+ * trial quantisation). */
+typedef struct {
+    int32_t n_agents;                 /* >= 0; 0 is a no-op */
+    int32_t layer_count;              /* >= 0 */
+    int32_t n_q_heads;                /* multiple of n_kv_heads */
+    int32_t n_kv_heads;               /* >= 1 */
+    int32_t head_dim;                 /* 64 or 128 */
+    float softmax_scale;              /* 0 => 1 / sqrt(head_dim) */
+    int32_t n_recent;                 /* recent query steps per agent (>= 1) */
+    const void* q;                    /* device [n_recent][n_agents][layer_count][n_q_heads][head_dim] */
+    pkv_dtype q_dtype;                /* PKV_F32 or PKV_BF16 */
+    const void* win_k;                /* device [n_agents][layer_count][n_kv_heads][win_cap][head_dim]:
+                                         the agents' native windows (the decode call's suffix buffers) */
+    const void* win_v;                /* same shape; both 16-byte aligned, may be NULL if every win_len is 0 */
+    pkv_dtype win_dtype;              /* PKV_F32 or PKV_BF16 */
+    int32_t win_cap;                  /* window capacity per agent */
+    const int32_t* win_len;           /* host [n_agents]: tokens of agent a's window used, 0 .. win_cap */
+    float* out;                       /* device fp32 [n_agents][layer_count] */
+} pkv_comix_args;
+
+/*
+ * Sensitivity s[a][l] = mean over agent a's recent query rows (n_recent steps
+ * x n_q_heads heads; head h uses kv head h / (n_q_heads / n_kv_heads)) of
+ * sum_t p_t ||v_t||, where p = softmax_t(sigma * q . k_t) over the first
+ * win_len[a] tokens of the agent's window in layer l (0 when win_len[a] = 0).
+ * With a V codec of mean relative squared error D_b, the mean attention-output
+ * error from quantising those values is at most sqrt(D_b) * s (triangle
+ * inequality, then Jensen), which is what comix_allocate_bits weighs.
+ * One workgroup per (agent, layer); deterministic (fixed summation order).
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP.
+ */
+int comix_sensitivity(const pkv_comix_args* args, void* stream);
+
+/*
+ * Joint V bit widths for n_items (agent, layer) items under a byte budget
+ * (CoMixKV news article: 2 to 4 bits allocated over all resident agents and
+ * layers under a shared budget with the real byte costs).  Host only.
+ *
+ * sensitivity: host [n_items], finite, >= 0 (e.g. comix_sensitivity's output);
+ * cost: host [n_items][3], bytes item i's next block takes at 2, 3, 4 bits,
+ * strictly increasing; error_factor: host [3], predicted error per unit of
+ * sensitivity at 2, 3, 4 bits, strictly decreasing, >= 0 (sqrt of
+ * pkv_lloyd_max_distortion for the bound above); bits: host [n_items] output.
+ * Rule: every item starts at 2 bits; repeatedly the single upgrade b -> b + 1
+ * with the largest s_i (e[b] - e[b+1]) / (cost_i[b+1] - cost_i[b]) is taken if
+ * it fits the remaining budget (ties: lower index), otherwise that item stays
+ * where it is; until no upgrade is left.  Returns PKV_ENOSPACE (bits
+ * untouched) if 2 bits everywhere exceed the budget; PKV_EINVAL on bad input.
+ */
+int comix_allocate_bits(int32_t n_items, const float* sensitivity, const uint64_t* cost,
+                        const double* error_factor, uint64_t budget, uint8_t* bits);
+
 /* ---- auxiliary queries (host only, no device work) ---- */
 
 /* Static text for a return code. */
@@ -205,7 +262,7 @@ const char* pkv_strerror(int code);
 int pkv_version(void);
 
 /* sizeof of the ABI structs, for bindings to check their mirrors:
- * which = 0: pkv_pool_config, 1: pkv_pool, 2: pkv_decode_args; else 0. */
+ * which = 0: pkv_pool_config, 1: pkv_pool, 2: pkv_decode_args, 3: pkv_comix_args; else 0. */
 size_t pkv_abi_sizeof(int32_t which);
 
 /*
@@ -215,6 +272,12 @@ size_t pkv_abi_sizeof(int32_t which);
  * Either pointer may be NULL.  Returns PKV_EUNSUPPORTED for other bits.
  */
 int pkv_lloyd_max_table(int32_t bits, float* centroids, float* thresholds);
+
+/*
+ * D_b = E[(X - Q(X))^2] for X ~ N(0, 1) and the library's fp32 table at
+ * `bits` in {2, 3, 4} (closed form per cell, in double); -1 for other bits.
+ */
+double pkv_lloyd_max_distortion(int32_t bits);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,326 @@
+// CoMixKV controller: per-(agent, layer) sensitivity from recent queries and the
+// native window, and joint 2/3/4-bit allocation under a byte budget.
+//
+// CoMixKV news article, abstract and method paragraphs: the controller builds
+// a local attention-error bound from the recently seen queries, keys and
+// values (no calibration data, no trial quantisation, no extra forward pass)
+// and allocates 2 to 4 bits jointly over every resident agent and layer under
+// one memory budget, with the real byte costs; new widths apply only to blocks
+// quantised afterwards.
+//
+// Bound used here: with local attention p_t = softmax_t(sigma q . k_t) over the
+// agent's native window and a V codec whose relative squared error has mean D_b
+// (the Lloyd-Max distortion of N(0, 1)), ||sum_t p_t (v_t - v_hat_t)|| <=
+// sum_t p_t ||v_t - v_hat_t||, whose mean is at most sqrt(D_b) sum_t p_t ||v_t||.
+// The sensitivity of (agent, layer) is sum_t p_t ||v_t|| averaged over the
+// agent's recent query rows (steps x query heads).
+//
+// k_comix_sens: one workgroup of 4 wavefronts per (agent, layer); wavefront w
+// takes kv heads w, w + 4, ...; for each, up to 32 query rows at a time are
+// staged in LDS (fp32) and the window is swept 4 tokens per step, 16 lanes per
+// token (D / 16 dimensions each): the score and ||v|| are lane sums over the 16
+// lanes, and every lane keeps an online (max, sum p, sum p ||v||) per row for its
+// token slot; the 4 slots are merged at the end.  Row values are summed in a
+// fixed order, then the 4 wavefronts' sums in LDS, so the result is
+// deterministic.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "pkv_internal.h"
+#include "pkv_lanes.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kComixAgents = 256;  // agents per launch (their window lengths travel in the arguments)
+constexpr int kComixRows = 32;     // query rows staged per pass
+
+struct ComixLaunch {
+    const void* q;
+    const void* win_k;
+    const void* win_v;
+    float* out;
+    int q_bf16, win_bf16;
+    int n_agents, agent0, n_agents_total, lc, hq, hkv, G, cap, n_recent;
+    float sm_log2;
+    float inv_rows;
+    int32_t len[kComixAgents];
+};
+
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// DL consecutive elements (bf16 or fp32) starting at element `off` of `base`, as floats
+template <int DL>
+__device__ __forceinline__ void load_row_part(const void* base, uint64_t off, bool bf16, float (&x)[DL]) {
+    if (bf16) {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+        if constexpr (DL == 8) {
+            const uint4 w = *reinterpret_cast<const uint4*>(p);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(u[i] << 16);
+                x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+            }
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(p);
+            const uint32_t u[2] = {w.x, w.y};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                x[2 * i] = __uint_as_float(u[i] << 16);
+                x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+            }
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+        for (int i = 0; i < DL / 4; ++i) {
+            const float4 f = p[i];
+            x[4 * i] = f.x;
+            x[4 * i + 1] = f.y;
+            x[4 * i + 2] = f.z;
+            x[4 * i + 3] = f.w;
+        }
+    }
+}
+
+__device__ __forceinline__ float sum16(float v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<8>(v);
+    return v;
+}
+
+// (m, l, u) of one row: l = sum 2^(s - m), u = sum 2^(s - m) * ||v||; m = -inf: empty
+__device__ __forceinline__ void merge_state(float& m, float& l, float& u, float m2, float l2, float u2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    const float a1 = exp2f(m - M), a2 = exp2f(m2 - M);  // exp2(-inf) = 0 for an empty side
+    l = l * a1 + l2 * a2;
+    u = u * a1 + u2 * a2;
+    m = M;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
+    constexpr int DL = D / 16;  // dimensions per lane
+    __shared__ float qs[4][kComixRows][D];
+    __shared__ float wsum[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kl = blockIdx.x / a.lc;  // agent within the launch
+    const int lj = blockIdx.x % a.lc;
+    const int k = a.agent0 + kl;
+    const int n = a.len[kl];
+    const int tl = lane >> 4, dl = lane & 15;
+    const int NR = a.n_recent * a.G;
+
+    float total = 0.0f;  // this wavefront's sum of row values, fixed order
+    if (n > 0) {
+        for (int g = wave; g < a.hkv; g += 4) {
+            const uint64_t wrow = (((uint64_t)k * a.lc + lj) * a.hkv + g) * (uint64_t)a.cap;
+            for (int rc = 0; rc < NR; rc += kComixRows) {
+                const int nrc = min(kComixRows, NR - rc);
+                // stage rows rc .. rc + nrc - 1 of this kv head: row j -> (step j / G, head g G + j % G)
+                for (int e = lane; e < nrc * D; e += 64) {
+                    const int j = rc + e / D, i = e % D;
+                    const int r = j / a.G, h = g * a.G + j % a.G;
+                    const uint64_t qo = ((((uint64_t)r * a.n_agents_total + k) * a.lc + lj) * a.hq + h) * D + i;
+                    qs[wave][e / D][i] = a.q_bf16 ? bf16_to_f(static_cast<const uint16_t*>(a.q)[qo])
+                                                  : static_cast<const float*>(a.q)[qo];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+                float m[kComixRows], l[kComixRows], u[kComixRows];
+#pragma unroll
+                for (int j = 0; j < kComixRows; ++j) {
+                    m[j] = -INFINITY;
+                    l[j] = 0.0f;
+                    u[j] = 0.0f;
+                }
+                for (int t0 = 0; t0 < n; t0 += 4) {
+                    const int t = t0 + tl;
+                    const bool ok = t < n;
+                    const uint64_t off = (wrow + (uint64_t)min(t, n - 1)) * D + (uint64_t)dl * DL;
+                    float kx[DL], vx[DL];
+                    load_row_part<DL>(a.win_k, off, a.win_bf16, kx);
+                    load_row_part<DL>(a.win_v, off, a.win_bf16, vx);
+                    float vv = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < DL; ++i) vv = fmaf(vx[i], vx[i], vv);
+                    const float vn = sqrtf(sum16(vv));
+#pragma unroll
+                    for (int j = 0; j < kComixRows; ++j) {
+                        if (j < nrc) {
+                            const float* qr = &qs[wave][j][dl * DL];
+                            float s = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < DL; ++i) s = fmaf(kx[i], qr[i], s);
+                            s = sum16(s) * a.sm_log2;
+                            if (ok) {
+                                const float mn = fmaxf(m[j], s);
+                                const float al = exp2f(m[j] - mn), e = exp2f(s - mn);
+                                l[j] = l[j] * al + e;
+                                u[j] = u[j] * al + e * vn;
+                                m[j] = mn;
+                            }
+                        }
+                    }
+                }
+                // merge the 4 token slots (lanes 16 apart), then sum the rows in order
+#pragma unroll
+                for (int j = 0; j < kComixRows; ++j) {
+                    if (j < nrc) {
+                        merge_state(m[j], l[j], u[j], lane_xor<16>(m[j]), lane_xor<16>(l[j]), lane_xor<16>(u[j]));
+                        merge_state(m[j], l[j], u[j], lane_xor<32>(m[j]), lane_xor<32>(l[j]), lane_xor<32>(u[j]));
+                        total += l[j] > 0.0f ? u[j] / l[j] : 0.0f;
+                    }
+                }
+                // the next pass overwrites this wavefront's rows (LDS operations of a wavefront
+                // complete in order; the fences keep the compiler from moving them)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+    }
+    if (lane == 0) wsum[wave] = total;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        a.out[(uint64_t)k * a.lc + lj] = n > 0 ? ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) * a.inv_rows : 0.0f;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+int comix_sensitivity(const pkv_comix_args* x, void* stream) {
+    using namespace pkv;
+    if (!x) return PKV_EINVAL;
+    if (x->n_agents < 0 || x->layer_count < 0 || x->n_kv_heads < 1 || x->n_q_heads < 1 || x->n_recent < 1)
+        return PKV_EINVAL;
+    if (x->n_q_heads % x->n_kv_heads) return PKV_EINVAL;
+    if (x->head_dim != 64 && x->head_dim != 128) return PKV_EUNSUPPORTED;
+    if ((x->q_dtype != PKV_F32 && x->q_dtype != PKV_BF16) || (x->win_dtype != PKV_F32 && x->win_dtype != PKV_BF16))
+        return PKV_EUNSUPPORTED;
+    if (!(x->softmax_scale >= 0.0f) || std::isinf(x->softmax_scale)) return PKV_EINVAL;
+    if (x->n_agents == 0 || x->layer_count == 0) return PKV_OK;
+    if (!x->q || !x->out || !x->win_len || x->win_cap < 0) return PKV_EINVAL;
+    bool any = false;
+    for (int a = 0; a < x->n_agents; ++a) {
+        if (x->win_len[a] < 0 || x->win_len[a] > x->win_cap) return PKV_EINVAL;
+        any |= x->win_len[a] > 0;
+    }
+    if (any && (!x->win_k || !x->win_v)) return PKV_EINVAL;
+    // window rows are read in 8- or 16-byte pieces
+    const uintptr_t mask = 15u;
+    if ((reinterpret_cast<uintptr_t>(x->win_k) & mask) || (reinterpret_cast<uintptr_t>(x->win_v) & mask) ||
+        (reinterpret_cast<uintptr_t>(x->out) & 3u))
+        return PKV_EINVAL;
+    ComixLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    L.q = x->q;
+    L.win_k = x->win_k;
+    L.win_v = x->win_v;
+    L.out = x->out;
+    L.q_bf16 = x->q_dtype == PKV_BF16;
+    L.win_bf16 = x->win_dtype == PKV_BF16;
+    L.n_agents_total = x->n_agents;
+    L.lc = x->layer_count;
+    L.hq = x->n_q_heads;
+    L.hkv = x->n_kv_heads;
+    L.G = x->n_q_heads / x->n_kv_heads;
+    L.cap = x->win_cap;
+    L.n_recent = x->n_recent;
+    const float sigma = x->softmax_scale > 0.0f ? x->softmax_scale : 1.0f / std::sqrt((float)x->head_dim);
+    L.sm_log2 = sigma * 1.4426950408889634f;
+    L.inv_rows = 1.0f / ((float)x->n_recent * (float)x->n_q_heads);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int a0 = 0; a0 < x->n_agents; a0 += kComixAgents) {
+        L.agent0 = a0;
+        L.n_agents = std::min(kComixAgents, x->n_agents - a0);
+        for (int i = 0; i < L.n_agents; ++i) L.len[i] = x->win_len[a0 + i];
+        const dim3 grid((unsigned)(L.n_agents * L.lc));
+        if (x->head_dim == 128) hipLaunchKernelGGL(k_comix_sens<128>, grid, dim3(256), 0, s, L);
+        else hipLaunchKernelGGL(k_comix_sens<64>, grid, dim3(256), 0, s, L);
+    }
+    return launch_status();
+}
+
+int comix_allocate_bits(int32_t n_items, const float* sensitivity, const uint64_t* cost, const double* error_factor,
+                        uint64_t budget, uint8_t* bits) {
+    if (n_items < 0) return PKV_EINVAL;
+    if (n_items == 0) return PKV_OK;
+    if (!sensitivity || !cost || !error_factor || !bits) return PKV_EINVAL;
+    if (!(error_factor[0] > error_factor[1] && error_factor[1] > error_factor[2] && error_factor[2] >= 0.0) ||
+        !std::isfinite(error_factor[0]))
+        return PKV_EINVAL;
+    uint64_t used = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const float si = sensitivity[i];
+        if (!(si >= 0.0f) || std::isinf(si)) return PKV_EINVAL;
+        const uint64_t* c = cost + 3 * (size_t)i;
+        if (!(c[0] < c[1] && c[1] < c[2])) return PKV_EINVAL;
+        if (used > UINT64_MAX - c[2]) return PKV_EINVAL;  // totals must fit 64 bits
+        used += c[0];
+    }
+    if (used > budget) return PKV_ENOSPACE;
+    std::vector<uint8_t> b(n_items, 2), frozen(n_items, 0);
+    // repeatedly the upgrade b -> b + 1 with the largest error decrease per added byte (ties:
+    // lower index); if it does not fit the remaining budget the item is not upgraded further
+    for (;;) {
+        int best = -1;
+        double best_ratio = -1.0;
+        for (int i = 0; i < n_items; ++i) {
+            if (frozen[i] || b[i] == 4) continue;
+            const int k = b[i] - 2;
+            const uint64_t* c = cost + 3 * (size_t)i;
+            const double gain = (double)sensitivity[i] * (error_factor[k] - error_factor[k + 1]);
+            const double ratio = gain / (double)(c[k + 1] - c[k]);
+            if (ratio > best_ratio) {
+                best = i;
+                best_ratio = ratio;
+            }
+        }
+        if (best < 0) break;
+        const int k = b[best] - 2;
+        const uint64_t dc = cost[3 * (size_t)best + k + 1] - cost[3 * (size_t)best + k];
+        if (dc <= budget - used) {
+            used += dc;
+            ++b[best];
+        } else {
+            frozen[best] = 1;
+        }
+    }
+    std::memcpy(bits, b.data(), (size_t)n_items);
+    return PKV_OK;
+}
+
+double pkv_lloyd_max_distortion(int32_t bits) {
+    if (bits < 2 || bits > 4) return -1.0;
+    // E[(X - Q(X))^2] for X ~ N(0, 1) over the fp32 table: on the cell (a, b] with
+    // output c, the integral of (x - c)^2 phi(x) dx is
+    // (1 + c^2)(Phi(b) - Phi(a)) - (b phi(b) - a phi(a)) + 2 c (phi(b) - phi(a))
+    const pkv::CodebookTables& t = pkv::codebook_tables();
+    const int n = 1 << bits;
+    const double rs2 = 1.0 / std::sqrt(2.0), rs2pi = 1.0 / std::sqrt(2.0 * M_PI);
+    auto phi = [&](double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * rs2pi; };
+    auto xphi = [&](double x) { return std::isinf(x) ? 0.0 : x * phi(x); };
+    auto Phi = [&](double x) { return 0.5 * std::erfc(-x * rs2); };
+    double d = 0.0;
+    for (int j = 0; j < n; ++j) {
+        const double lo = j == 0 ? -INFINITY : (double)t.thr[bits - 2][j - 1];
+        const double hi = j == n - 1 ? INFINITY : (double)t.thr[bits - 2][j];
+        const double c = (double)t.cent[bits - 2][j];
+        d += (1.0 + c * c) * (Phi(hi) - Phi(lo)) - (xphi(hi) - xphi(lo)) + 2.0 * c * (phi(hi) - phi(lo));
+    }
+    return d;
+}
+
+}  // extern "C"

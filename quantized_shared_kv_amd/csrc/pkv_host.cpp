@@ -156,13 +156,14 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 101; }
+int pkv_version(void) { return 102; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {
         case 0: return sizeof(pkv_pool_config);
         case 1: return sizeof(pkv_pool);
         case 2: return sizeof(pkv_decode_args);
+        case 3: return sizeof(pkv_comix_args);
         default: return 0;
     }
 }

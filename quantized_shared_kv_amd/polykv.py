@@ -14,7 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
-ABI_VERSION = 101  # pkv_version() of the library these ctypes mirrors describe
+ABI_VERSION = 102  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -49,6 +49,13 @@ class DecodeArgs(ctypes.Structure):
                 ("pool_events", POINTER(c_void_p)), ("agent_private_pool", POINTER(POINTER(Pool)))]
 
 
+class ComixArgs(ctypes.Structure):
+    _fields_ = [("n_agents", c_int32), ("layer_count", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("softmax_scale", c_float), ("n_recent", c_int32), ("q", c_void_p),
+                ("q_dtype", c_int32), ("win_k", c_void_p), ("win_v", c_void_p), ("win_dtype", c_int32),
+                ("win_cap", c_int32), ("win_len", POINTER(c_int32)), ("out", c_void_p)]
+
+
 _LIB = None
 
 
@@ -75,7 +82,14 @@ def lib() -> ctypes.CDLL:
         L.pkv_abi_sizeof.restype = c_size_t
         L.pkv_lloyd_max_table.argtypes = [c_int32, POINTER(c_float), POINTER(c_float)]
         L.pkv_lloyd_max_table.restype = c_int32
-        for i, s in enumerate((PoolConfig, Pool, DecodeArgs)):
+        L.pkv_lloyd_max_distortion.argtypes = [c_int32]
+        L.pkv_lloyd_max_distortion.restype = ctypes.c_double
+        L.comix_sensitivity.argtypes = [POINTER(ComixArgs), c_void_p]
+        L.comix_sensitivity.restype = c_int32
+        L.comix_allocate_bits.argtypes = [c_int32, POINTER(c_float), POINTER(c_uint64), POINTER(ctypes.c_double),
+                                          c_uint64, POINTER(c_uint8)]
+        L.comix_allocate_bits.restype = c_int32
+        for i, s in enumerate((PoolConfig, Pool, DecodeArgs, ComixArgs)):
             if L.pkv_abi_sizeof(i) != ctypes.sizeof(s):
                 raise ImportError(f"ABI mismatch for {s.__name__}")
         if L.pkv_version() != ABI_VERSION:
@@ -207,3 +221,43 @@ def lloyd_max_table(bits: int):
     t = (c_float * 15)()
     _check(lib().pkv_lloyd_max_table(bits, c, t), "pkv_lloyd_max_table")
     return list(c[: 1 << bits]), list(t[: (1 << bits) - 1])
+
+
+def lloyd_max_distortion(bits: int) -> float:
+    """The library's D_b = E[(X - Q(X))^2] for N(0, 1) at `bits` (2, 3, 4)."""
+    d = lib().pkv_lloyd_max_distortion(bits)
+    if d < 0:
+        raise PolyKVError(-2, "pkv_lloyd_max_distortion")
+    return float(d)
+
+
+def comix_sensitivity(q, win_k, win_v, win_len, out, softmax_scale=0.0, stream=None) -> None:
+    """Enqueue the CoMixKV sensitivity estimate.
+
+    q: [n_recent][A][L][Hq][d] (bf16 or fp32); win_k, win_v: [A][L][Hkv][cap][d] (bf16 or
+    fp32, the agents' native windows); win_len: A ints; out: fp32 [A][L].
+    """
+    R, A, L, Hq, d = q.shape
+    if not q.is_contiguous() or not out.is_contiguous() or tuple(out.shape) != (A, L) or out.dtype.itemsize != 4:
+        raise ValueError("q must be contiguous [R][A][L][Hq][d]; out contiguous fp32 [A][L]")
+    if win_k is None or win_v is None:
+        raise ValueError("windows required")
+    if not (win_k.is_contiguous() and win_v.is_contiguous()) or win_k.shape != win_v.shape or \
+            win_k.dim() != 5 or tuple(win_k.shape[:2]) != (A, L) or win_k.shape[4] != d or win_k.dtype != win_v.dtype:
+        raise ValueError("windows must be contiguous [A][L][Hkv][cap][d], same shape and dtype")
+    lens = (c_int32 * A)(*[int(x) for x in win_len])
+    a = ComixArgs(A, L, Hq, int(win_k.shape[2]), d, float(softmax_scale), R, c_void_p(q.data_ptr()), _dtype_code(q),
+                  c_void_p(win_k.data_ptr()), c_void_p(win_v.data_ptr()), _dtype_code(win_k), int(win_k.shape[3]),
+                  lens, c_void_p(out.data_ptr()))
+    _check(lib().comix_sensitivity(ctypes.byref(a), c_void_p(_stream_handle(stream))), "comix_sensitivity")
+
+
+def comix_allocate_bits(sensitivity, cost, error_factor, budget: int):
+    """Bits (2..4) per item; sensitivity [n] floats, cost [n][3] byte counts, error_factor [3]."""
+    n = len(sensitivity)
+    s = (c_float * max(n, 1))(*[float(x) for x in sensitivity])
+    c = (c_uint64 * max(3 * n, 1))(*[int(x) for row in cost for x in row])
+    e = (ctypes.c_double * 3)(*[float(x) for x in error_factor])
+    out = (c_uint8 * max(n, 1))()
+    _check(lib().comix_allocate_bits(n, s, c, e, int(budget), out), "comix_allocate_bits")
+    return [int(out[i]) for i in range(n)]

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"pool_bytes", "pool_build", "pool_quantize_append", "agent_decode_attention"}
+    assert set(names) >= {"pool_bytes", "pool_build", "pool_quantize_append", "agent_decode_attention",
+                          "comix_sensitivity", "comix_allocate_bits", "pkv_lloyd_max_distortion"}
     lib = pk.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -38,7 +39,8 @@ def test_struct_mirrors_match_c_sizes():
     assert lib.pkv_abi_sizeof(0) == ctypes.sizeof(pk.PoolConfig)
     assert lib.pkv_abi_sizeof(1) == ctypes.sizeof(pk.Pool)
     assert lib.pkv_abi_sizeof(2) == ctypes.sizeof(pk.DecodeArgs)
-    assert lib.pkv_abi_sizeof(3) == 0
+    assert lib.pkv_abi_sizeof(3) == ctypes.sizeof(pk.ComixArgs)
+    assert lib.pkv_abi_sizeof(4) == 0
     assert lib.pkv_version() == pk.ABI_VERSION
 
 

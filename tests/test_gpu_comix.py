@@ -1,0 +1,127 @@
+"""GPU parity of the CoMixKV sensitivity kernel and the controller end to end.
+
+comix_sensitivity (one workgroup per (agent, layer), fp32 online softmax over
+the native window) against the oracle's fp64 definition: small ragged cases
+(empty, one-token and odd windows, GQA 4 and 8, MHA d 64, fp32 and bf16, more
+than 32 query rows per kv head), and sampled entries at the Qwen3-32B shape
+(8 agents, 64 layers, 64/8 heads, 128-token windows, 8 recent steps).  Then
+the allocation on the device-measured sensitivities equals the oracle's
+allocation on the oracle's sensitivities whenever their greedy choices are not
+within rounding of a tie.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import comixkv
+from quantized_shared_kv_amd import polykv as pk
+
+from gpu_helpers import DEV, to_device
+
+pytestmark = pytest.mark.gpu
+RTOL = 2e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    pk.lib()
+
+
+def _inputs(w, R, dtype):
+    """Recent queries [R][A][L][Hq][d] and windows [A][L][Hkv][S][d] from the workload's seeded slices."""
+    A, L = w.n_agents, w.n_layers
+    q = torch.stack([torch.stack([to_device(w.queries(r, a)) for a in range(A)]) for r in range(R)]).contiguous()
+    k = torch.stack([torch.stack([to_device(w.sfx_k(a, l)) for l in range(L)]) for a in range(A)]).contiguous()
+    v = torch.stack([torch.stack([to_device(w.sfx_v(a, l)) for l in range(L)]) for a in range(A)]).contiguous()
+    if dtype == "f32":
+        q, k, v = q.float(), k.float(), v.float()
+    return q, k, v
+
+
+CASES = {
+    "g4_bf16_ragged": (wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=8, n_agents=3, sfx_tokens=37),
+                       3, [37, 0, 5], "bf16"),
+    "mha_d64_f32": (wl.SMOLLM2.replace(n_layers=2, n_q_heads=4, n_kv_heads=4, n_agents=2, sfx_tokens=64),
+                    2, [1, 64], "f32"),
+    "g8_40_rows": (wl.QWEN3_32B_MIXED.replace(n_layers=2, n_agents=2, sfx_tokens=50), 5, [50, 13], "bf16"),
+    "g8_d64_bf16": (wl.SMOLLM2.replace(n_layers=3, n_q_heads=16, n_kv_heads=2, n_agents=2, sfx_tokens=9),
+                    1, [9, 4], "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_sensitivity_matches_oracle(name):
+    w, R, lens, dtype = CASES[name]
+    print(f"[comix] case {name}", flush=True)
+    q, k, v = _inputs(w, R, dtype)
+    out = torch.full((w.n_agents, w.n_layers), float("nan"), dtype=torch.float32, device=DEV)
+    pk.comix_sensitivity(q, k, v, lens, out)
+    torch.cuda.synchronize()
+    want = comixkv.sensitivity(q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy(), lens,
+                               w.n_kv_heads)
+    got = out.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=RTOL, atol=0)
+    assert np.all(got[np.array(lens) == 0] == 0.0)
+    # deterministic: a second call writes the same bits
+    out2 = torch.empty_like(out)
+    pk.comix_sensitivity(q, k, v, lens, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_sensitivity_qwen3_32b_shape_sampled():
+    """Full Qwen3-32B CoMixKV shape: device-seeded windows and queries, 12 sampled (agent, layer) checked."""
+    A, L, Hq, Hkv, d, S, R = 8, 64, 64, 8, 128, 128, 8
+    print("[comix] qwen3-32b shape", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    q = torch.randn((R, A, L, Hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    scale = torch.exp(0.5 * torch.randn((1, L, Hkv, 1, d), generator=g, device=DEV))
+    k = (torch.randn((A, L, Hkv, S, d), generator=g, device=DEV) * scale).to(torch.bfloat16)
+    v = (torch.randn((A, L, Hkv, S, d), generator=g, device=DEV) * scale.flip(1)).to(torch.bfloat16)
+    lens = [128, 1, 77, 128, 0, 64, 128, 5]
+    out = torch.empty((A, L), dtype=torch.float32, device=DEV)
+    pk.comix_sensitivity(q, k, v, lens, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got)) and np.all(got[4] == 0.0) and np.all(got >= 0)
+    rng = np.random.default_rng(0)
+    for a, l in zip(rng.integers(0, A, 12), rng.integers(0, L, 12)):
+        want = comixkv.sensitivity(q[:, a:a + 1, l:l + 1].float().cpu().numpy(),
+                                   k[a:a + 1, l:l + 1].float().cpu().numpy(),
+                                   v[a:a + 1, l:l + 1].float().cpu().numpy(), [lens[a]], Hkv)[0, 0]
+        assert abs(got[a, l] - want) <= RTOL * max(want, 1e-30), (a, l, got[a, l], want)
+
+
+def test_controller_end_to_end_matches_oracle():
+    """Sensitivities on the device, bits from the library, against the oracle's on its own sensitivities."""
+    w, R, lens, _ = CASES["g8_40_rows"]
+    w = w.replace(n_layers=6, n_agents=3)
+    lens = [50, 31, 8]
+    q, k, v = _inputs(w, R, "bf16")
+    out = torch.empty((w.n_agents, w.n_layers), dtype=torch.float32, device=DEV)
+    pk.comix_sensitivity(q, k, v, lens, out)
+    torch.cuda.synchronize()
+    s_dev = out.cpu().numpy().ravel()
+    s_ref = comixkv.sensitivity(q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy(), lens,
+                                w.n_kv_heads).ravel()
+    cost = np.stack([comixkv.block_cost(256, w.n_kv_heads, w.head_dim)] * s_dev.size)
+    err = [pk.lloyd_max_distortion(b) ** 0.5 for b in (2, 3, 4)]
+    budget = int(cost[:, 1].sum())  # the bytes of 3 bits everywhere
+    bits = pk.comix_allocate_bits(s_dev, cost, err, budget)
+    want = comixkv.allocate(s_ref.astype(np.float32), cost, comixkv.error_factors(), budget)
+    # equal unless two items' upgrade gains (equal costs: s * (e[b] - e[b + 1])) are within the
+    # sensitivities' rounding of each other, which could order the greedy choices differently
+    e = comixkv.error_factors()
+    gains = sorted([(x * (e[0] - e[1]), i) for i, x in enumerate(s_ref)] + [(x * (e[1] - e[2]), i) for i, x in enumerate(s_ref)])
+    close = any(i != j and abs(x - y) <= 1e-4 * max(x, y) for (x, i), (y, j) in zip(gains, gains[1:]))
+    if not close:
+        assert bits == list(want)
+    assert int(cost[np.arange(s_dev.size), np.array(bits) - 2].sum()) <= budget
+    assert comixkv.objective(s_ref, comixkv.error_factors(), bits) <= comixkv.objective(
+        s_ref, comixkv.error_factors(), [3] * s_dev.size) + 1e-12
