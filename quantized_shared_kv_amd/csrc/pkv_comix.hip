@@ -17,12 +17,14 @@
 //
 // k_comix_sens: one workgroup of 4 wavefronts per (agent, layer); wavefront w
 // takes kv heads w, w + 4, ...; for each, up to 32 query rows at a time are
-// staged in LDS (fp32) and the window is swept 4 tokens per step, 16 lanes per
-// token (D / 16 dimensions each): the score and ||v|| are lane sums over the 16
-// lanes, and every lane keeps an online (max, sum p, sum p ||v||) per row for its
-// token slot; the 4 slots are merged at the end.  Row values are summed in a
-// fixed order, then the 4 wavefronts' sums in LDS, so the result is
-// deterministic.
+// staged in LDS (fp32) and the window is swept 32 tokens at a time, two lanes
+// per token: lane half h holds the 16-byte chunks 2i + h of its token's key row
+// (fp32) and its ||v||, reads the same chunks of each query row from LDS (32
+// lanes per address: a broadcast, the two halves on different banks), and one
+// lane exchange completes the score; every lane keeps an online (max, sum p,
+// sum p ||v||) per row over the tokens it has seen, and the 32 token slots'
+// states are merged at the end.  Row values are summed in a fixed order,
+// then the 4 wavefronts' sums in LDS, so the result is deterministic.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -51,47 +53,31 @@ struct ComixLaunch {
 
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// DL consecutive elements (bf16 or fp32) starting at element `off` of `base`, as floats
-template <int DL>
-__device__ __forceinline__ void load_row_part(const void* base, uint64_t off, bool bf16, float (&x)[DL]) {
+// the 16-byte chunks 2i + h (i < D / 8) of row `t` of `base` (bf16 or fp32) as floats:
+// x[4 i .. 4 i + 3] = elements 4 (2 i + h) .. 4 (2 i + h) + 3
+template <int D>
+__device__ __forceinline__ void load_half_row(const void* base, uint64_t t, int h, bool bf16, float (&x)[D / 2]) {
     if (bf16) {
-        const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-        if constexpr (DL == 8) {
-            const uint4 w = *reinterpret_cast<const uint4*>(p);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + t * D);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = __uint_as_float(u[i] << 16);
-                x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-            }
-        } else {
-            const uint2 w = *reinterpret_cast<const uint2*>(p);
-            const uint32_t u[2] = {w.x, w.y};
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                x[2 * i] = __uint_as_float(u[i] << 16);
-                x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-            }
+        for (int i = 0; i < D / 8; ++i) {
+            const uint2 w = p[2 * i + h];
+            x[4 * i] = __uint_as_float(w.x << 16);
+            x[4 * i + 1] = __uint_as_float(w.x & 0xffff0000u);
+            x[4 * i + 2] = __uint_as_float(w.y << 16);
+            x[4 * i + 3] = __uint_as_float(w.y & 0xffff0000u);
         }
     } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + t * D);
 #pragma unroll
-        for (int i = 0; i < DL / 4; ++i) {
-            const float4 f = p[i];
+        for (int i = 0; i < D / 8; ++i) {
+            const float4 f = p[2 * i + h];
             x[4 * i] = f.x;
             x[4 * i + 1] = f.y;
             x[4 * i + 2] = f.z;
             x[4 * i + 3] = f.w;
         }
     }
-}
-
-__device__ __forceinline__ float sum16(float v) {
-    v += lane_xor<1>(v);
-    v += lane_xor<2>(v);
-    v += lane_xor<4>(v);
-    v += lane_xor<8>(v);
-    return v;
 }
 
 // (m, l, u) of one row: l = sum 2^(s - m), u = sum 2^(s - m) * ||v||; m = -inf: empty
@@ -104,10 +90,15 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float& u, float 
     m = M;
 }
 
+template <int M>
+__device__ __forceinline__ void merge_lanes(float& m, float& l, float& u) {
+    const float m2 = lane_xor<M>(m), l2 = lane_xor<M>(l), u2 = lane_xor<M>(u);
+    merge_state(m, l, u, m2, l2, u2);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
-    constexpr int DL = D / 16;  // dimensions per lane
-    __shared__ float qs[4][kComixRows][D];
+    __shared__ __align__(16) float qs[4][kComixRows][D];
     __shared__ float wsum[4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -115,7 +106,6 @@ __global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
     const int lj = blockIdx.x % a.lc;
     const int k = a.agent0 + kl;
     const int n = a.len[kl];
-    const int tl = lane >> 4, dl = lane & 15;
     const int NR = a.n_recent * a.G;
 
     float total = 0.0f;  // this wavefront's sum of row values, fixed order
@@ -143,25 +133,42 @@ __global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
                     l[j] = 0.0f;
                     u[j] = 0.0f;
                 }
-                for (int t0 = 0; t0 < n; t0 += 4) {
-                    const int t = t0 + tl;
+                const int hf = lane & 1, slot = lane >> 1;
+                for (int t0 = 0; t0 < n; t0 += 32) {
+                    const int t = t0 + slot;
                     const bool ok = t < n;
-                    const uint64_t off = (wrow + (uint64_t)min(t, n - 1)) * D + (uint64_t)dl * DL;
-                    float kx[DL], vx[DL];
-                    load_row_part<DL>(a.win_k, off, a.win_bf16, kx);
-                    load_row_part<DL>(a.win_v, off, a.win_bf16, vx);
-                    float vv = 0.0f;
+                    const uint64_t tt = wrow + (uint64_t)min(t, n - 1);  // past the window: a valid row, unused
+                    float vn;
+                    {
+                        float vx[D / 2];
+                        load_half_row<D>(a.win_v, tt, hf, a.win_bf16, vx);
+                        float vv = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < DL; ++i) vv = fmaf(vx[i], vx[i], vv);
-                    const float vn = sqrtf(sum16(vv));
+                        for (int i = 0; i < D / 2; ++i) vv = fmaf(vx[i], vx[i], vv);
+                        vn = sqrtf(vv + lane_xor<1>(vv));
+                    }
+                    asm volatile("" ::: "memory");  // the value half-row is dead before the key half-row loads
+                    float kx[D / 2];
+                    load_half_row<D>(a.win_k, tt, hf, a.win_bf16, kx);
 #pragma unroll
                     for (int j = 0; j < kComixRows; ++j) {
                         if (j < nrc) {
-                            const float* qr = &qs[wave][j][dl * DL];
-                            float s = 0.0f;
+                            const float4* qr = reinterpret_cast<const float4*>(&qs[wave][j][0]);
+                            float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-                            for (int i = 0; i < DL; ++i) s = fmaf(kx[i], qr[i], s);
-                            s = sum16(s) * a.sm_log2;
+                            for (int i = 0; i < D / 8; i += 2) {
+                                const float4 q0 = qr[2 * i + hf], q1 = qr[2 * i + 2 + hf];
+                                s0 = fmaf(kx[4 * i], q0.x, s0);
+                                s0 = fmaf(kx[4 * i + 1], q0.y, s0);
+                                s0 = fmaf(kx[4 * i + 2], q0.z, s0);
+                                s0 = fmaf(kx[4 * i + 3], q0.w, s0);
+                                s1 = fmaf(kx[4 * i + 4], q1.x, s1);
+                                s1 = fmaf(kx[4 * i + 5], q1.y, s1);
+                                s1 = fmaf(kx[4 * i + 6], q1.z, s1);
+                                s1 = fmaf(kx[4 * i + 7], q1.w, s1);
+                            }
+                            float s = s0 + s1;
+                            s = (s + lane_xor<1>(s)) * a.sm_log2;
                             if (ok) {
                                 const float mn = fmaxf(m[j], s);
                                 const float al = exp2f(m[j] - mn), e = exp2f(s - mn);
@@ -172,12 +179,16 @@ __global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
                         }
                     }
                 }
-                // merge the 4 token slots (lanes 16 apart), then sum the rows in order
+                // merge the 32 token slots' states (both lanes of a slot hold the same), then sum
+                // the rows in order
 #pragma unroll
                 for (int j = 0; j < kComixRows; ++j) {
                     if (j < nrc) {
-                        merge_state(m[j], l[j], u[j], lane_xor<16>(m[j]), lane_xor<16>(l[j]), lane_xor<16>(u[j]));
-                        merge_state(m[j], l[j], u[j], lane_xor<32>(m[j]), lane_xor<32>(l[j]), lane_xor<32>(u[j]));
+                        merge_lanes<2>(m[j], l[j], u[j]);
+                        merge_lanes<4>(m[j], l[j], u[j]);
+                        merge_lanes<8>(m[j], l[j], u[j]);
+                        merge_lanes<16>(m[j], l[j], u[j]);
+                        merge_lanes<32>(m[j], l[j], u[j]);
                         total += l[j] > 0.0f ? u[j] / l[j] : 0.0f;
                     }
                 }
@@ -218,7 +229,7 @@ int comix_sensitivity(const pkv_comix_args* x, void* stream) {
         any |= x->win_len[a] > 0;
     }
     if (any && (!x->win_k || !x->win_v)) return PKV_EINVAL;
-    // window rows are read in 8- or 16-byte pieces
+    // window rows are read in 16-byte pieces
     const uintptr_t mask = 15u;
     if ((reinterpret_cast<uintptr_t>(x->win_k) & mask) || (reinterpret_cast<uintptr_t>(x->win_v) & mask) ||
         (reinterpret_cast<uintptr_t>(x->out) & 3u))
