@@ -13,6 +13,7 @@ stream around the kernel, and the CPU oracle timed on a bounded sample of the
 same work.  Only the ``cpu_baseline`` leg imports the oracle.
 
     python bench.py [--steps K] [--warmup W] [--kernel valu|mfma|default] [--no-cpu-baseline]
+    python bench.py --comix      (the CoMixKV controller instead: its own JSON line)
 """
 from __future__ import annotations
 
@@ -42,6 +43,9 @@ def parse():
                     help="extra untimed pool-kernel launches, each after a 512 MiB cache flush")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                             "pool_decode_traffic.json"))
+    ap.add_argument("--comix", action="store_true",
+                    help="instead of the decode job: time the CoMixKV controller (sensitivity kernel + allocation) "
+                         "on the Qwen3-32B shape and measure the attention error of its bits against uniform 3 bits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -120,6 +124,9 @@ def main():
 
         pmc_summary(args.pmc_summary, args.traffic_json, "valu" if args.kernel == "valu" else "mfma",
                     wl.LLAMA3_8B.name)
+        return
+    if args.comix:
+        comix_bench()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
@@ -303,6 +310,114 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, steps_per_job)
     print(json.dumps(line), flush=True)
+
+
+def comix_bench():
+    """CoMixKV controller on the Qwen3-32B shape (8 agents, 64 layers, 64/8 heads, d 128).
+
+    Each agent has a 128-token native window and 8 recent query steps (device-seeded
+    bf16: K, V = N(0, 1) * sigma, sigma ~ LogNormal(0, 0.5) per (layer, kv head, channel);
+    the second recipe also scales V by a per-(agent, layer) factor ~ LogNormal(0, 1)).
+    Timed: comix_sensitivity (HIP events) and comix_allocate_bits (host).  Checked: with the
+    budget of 3 bits everywhere, each agent's window is quantized into its own pool at the
+    allocated per-layer widths and at uniform 3 bits, the recent queries are decoded over
+    it, and the outputs are compared with exact attention over the bf16 window (the same
+    decode call with an empty pool and the window as native suffix).
+    """
+    import torch
+
+    from quantized_shared_kv_amd import polykv as pk
+
+    pk.lib()
+    dev = "cuda:0"
+    A, L, Hq, Hkv, d, S, R = 8, 64, 64, 8, 128, 128, 8
+    err = [pk.lloyd_max_distortion(b) ** 0.5 for b in (2, 3, 4)]
+    cost_row = [S * (Hkv * (d + d * b // 8 + 4) + 4) for b in (2, 3, 4)]  # one layer of one agent's block
+    budget = A * L * cost_row[1]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for recipe in ("channel_lognormal", "channel_and_layer_lognormal"):
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        q = torch.randn((R, A, L, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+        sk = torch.exp(0.5 * torch.randn((1, L, Hkv, 1, d), generator=g, device=dev))
+        sv = torch.exp(0.5 * torch.randn((1, L, Hkv, 1, d), generator=g, device=dev))
+        if recipe != "channel_lognormal":
+            sv = sv * torch.exp(torch.randn((A, L, 1, 1, 1), generator=g, device=dev))
+        wk = (torch.randn((A, L, Hkv, S, d), generator=g, device=dev) * sk).to(torch.bfloat16)
+        wv = (torch.randn((A, L, Hkv, S, d), generator=g, device=dev) * sv).to(torch.bfloat16)
+        sens = torch.empty((A, L), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            pk.comix_sensitivity(q, wk, wv, [S] * A, sens)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            pk.comix_sensitivity(q, wk, wv, [S] * A, sens)
+        e1.record()
+        torch.cuda.synchronize()
+        sens_us = 1e3 * e0.elapsed_time(e1) / 10
+        s_host = sens.cpu().numpy().ravel()
+        t0 = time.perf_counter()
+        bits = pk.comix_allocate_bits(s_host, [cost_row] * (A * L), err, budget)
+        alloc_us = 1e6 * (time.perf_counter() - t0)
+        bits = np.array(bits).reshape(A, L)
+
+        def decode_error(bits_al):
+            bufs, pools = [], []
+            for a in range(A):
+                cfg = pk.make_config(L, Hkv, d, S, [int(b) for b in bits_al[a]])
+                n = pk.pool_bytes(cfg)
+                bufs.append(torch.empty(n, dtype=torch.uint8, device=dev))
+                pools.append(pk.pool_build(cfg, bufs[-1].data_ptr(), n))
+                pk.pool_quantize_append(pools[-1], 0, wk[a].contiguous(), wv[a].contiguous())
+            empty_cfg = pk.make_config(L, Hkv, d, S, [3] * L)
+            ne = pk.pool_bytes(empty_cfg)
+            ebufs = [torch.empty(ne, dtype=torch.uint8, device=dev) for _ in range(A)]
+            empty = [pk.pool_build(empty_cfg, b.data_ptr(), ne) for b in ebufs]
+            out = torch.empty((A, L, Hq, d), dtype=torch.float32, device=dev)
+            ref = torch.empty_like(out)
+            wsb = max(pk.agent_decode_attention(pools, q[0], out, 0),
+                      pk.agent_decode_attention(empty, q[0], ref, 0, wk, wv, [S] * A))
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            rel_sum = torch.zeros((A, L), dtype=torch.float64, device=dev)
+            abs_sum = torch.zeros((A, L), dtype=torch.float64, device=dev)
+            for r in range(R):
+                pk.agent_decode_attention(pools, q[r], out, 0, workspace=ws)
+                pk.agent_decode_attention(empty, q[r], ref, 0, wk, wv, [S] * A, workspace=ws)
+                diff = (out - ref).double().norm(dim=-1)
+                rel_sum += (diff / ref.double().norm(dim=-1)).mean(dim=-1)
+                abs_sum += diff.mean(dim=-1)
+            torch.cuda.synchronize()
+            return (rel_sum / R).cpu().numpy(), (abs_sum / R).cpu().numpy()
+
+        e_alloc, a_alloc = decode_error(bits)
+        e_uni, a_uni = decode_error(np.full((A, L), 3))
+        s64 = s_host.astype(np.float64)
+        res[recipe] = {
+            "sensitivity_us": sens_us, "allocate_us": alloc_us,
+            "bits_hist": {str(b): int(np.sum(bits == b)) for b in (2, 3, 4)},
+            "bytes": {"budget": budget, "used": int(sum(cost_row[b - 2] for b in bits.ravel()))},
+            "predicted_error_sum": {"uniform_3bit": float(np.sum(s64 * err[1])),
+                                    "allocated": float(np.sum(s64 * np.array(err)[bits.ravel() - 2]))},
+            "attention_abs_error_sum": {"uniform_3bit": float(a_uni.sum()), "allocated": float(a_alloc.sum())},
+            "attention_rel_error_mean": {"uniform_3bit": float(e_uni.mean()), "allocated": float(e_alloc.mean())},
+            "attention_rel_error_worst_item": {"uniform_3bit": float(e_uni.max()), "allocated": float(e_alloc.max())},
+        }
+        log(f"[comix] {recipe}: {json.dumps(res[recipe])}")
+    # sensitivity kernel roofline: fp32 multiply-adds of the scores and the ||v|| sums
+    flops = A * L * Hkv * (R * (Hq // Hkv) * S * d * 2 + S * d * 2)
+    first = res["channel_lognormal"]
+    print(json.dumps({"metric": "CoMixKV controller: sensitivity kernel time and allocation quality",
+                      "value": first["sensitivity_us"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
+                      "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": "qwen3_32b_comix_controller", "agents": A, "layers": L, "q_heads": Hq,
+                                 "kv_heads": Hkv, "head_dim": d, "window": S, "recent_steps": R,
+                                 "budget": "bytes of 3 bits everywhere"},
+                      "roofline": {"bound": "alu", "achieved": flops / (first["sensitivity_us"] * 1e-6) / 1e12,
+                                   "peak": 157.3, "unit": "TFLOP/s",
+                                   "frac": flops / (first["sensitivity_us"] * 1e-6) / 1e12 / 157.3,
+                                   "kernel": "comix sensitivity", "flops_per_launch": flops},
+                      "recipes": res}), flush=True)
 
 
 def cpu_baseline(w, steps_per_job):

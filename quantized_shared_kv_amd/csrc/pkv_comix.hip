@@ -282,31 +282,34 @@ int comix_allocate_bits(int32_t n_items, const float* sensitivity, const uint64_
         used += c[0];
     }
     if (used > budget) return PKV_ENOSPACE;
-    std::vector<uint8_t> b(n_items, 2), frozen(n_items, 0);
     // repeatedly the upgrade b -> b + 1 with the largest error decrease per added byte (ties:
-    // lower index); if it does not fit the remaining budget the item is not upgraded further
-    for (;;) {
-        int best = -1;
-        double best_ratio = -1.0;
-        for (int i = 0; i < n_items; ++i) {
-            if (frozen[i] || b[i] == 4) continue;
-            const int k = b[i] - 2;
-            const uint64_t* c = cost + 3 * (size_t)i;
-            const double gain = (double)sensitivity[i] * (error_factor[k] - error_factor[k + 1]);
-            const double ratio = gain / (double)(c[k + 1] - c[k]);
-            if (ratio > best_ratio) {
-                best = i;
-                best_ratio = ratio;
-            }
-        }
-        if (best < 0) break;
-        const int k = b[best] - 2;
-        const uint64_t dc = cost[3 * (size_t)best + k + 1] - cost[3 * (size_t)best + k];
-        if (dc <= budget - used) {
-            used += dc;
-            ++b[best];
-        } else {
-            frozen[best] = 1;
+    // lower index); if it does not fit the remaining budget the item is not upgraded further.
+    // A heap of each item's next upgrade, ordered by (ratio, then lower index), makes the same
+    // choices as scanning every item each time.
+    std::vector<uint8_t> b(n_items, 2);
+    auto ratio = [&](int i) {
+        const int k = b[i] - 2;
+        const uint64_t* c = cost + 3 * (size_t)i;
+        const double gain = (double)sensitivity[i] * (error_factor[k] - error_factor[k + 1]);
+        return gain / (double)(c[k + 1] - c[k]);
+    };
+    typedef std::pair<double, int> Cand;
+    auto worse = [](const Cand& x, const Cand& y) { return x.first < y.first || (x.first == y.first && x.second > y.second); };
+    std::vector<Cand> heap;
+    heap.reserve(n_items);
+    for (int i = 0; i < n_items; ++i) heap.push_back({ratio(i), i});
+    std::make_heap(heap.begin(), heap.end(), worse);
+    while (!heap.empty()) {
+        std::pop_heap(heap.begin(), heap.end(), worse);
+        const int i = heap.back().second;
+        heap.pop_back();
+        const int k = b[i] - 2;
+        const uint64_t dc = cost[3 * (size_t)i + k + 1] - cost[3 * (size_t)i + k];
+        if (dc > budget - used) continue;  // stays at b[i]
+        used += dc;
+        if (++b[i] < 4) {
+            heap.push_back({ratio(i), i});
+            std::push_heap(heap.begin(), heap.end(), worse);
         }
     }
     std::memcpy(bits, b.data(), (size_t)n_items);
