@@ -13,6 +13,7 @@ stream around the kernel, and the CPU oracle timed on a bounded sample of the
 same work.  Only the ``cpu_baseline`` leg imports the oracle.
 
     python bench.py [--steps K] [--warmup W] [--kernel valu|mfma|default] [--no-cpu-baseline]
+    python bench.py --workload qwen3_32b_comix   (8 agents, own mixed-bit pools; not the headline)
     python bench.py --comix      (the CoMixKV controller instead: its own JSON line)
 """
 from __future__ import annotations
@@ -43,6 +44,9 @@ def parse():
                     help="extra untimed pool-kernel launches, each after a 512 MiB cache flush")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                             "pool_decode_traffic.json"))
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "qwen3_32b_comix"],
+                    help="llama3_8b (default, the headline): one shared 4096-token pool, 15 agents; "
+                         "qwen3_32b_comix: 8 agents with their own 8064-token mixed 2/3/4-bit pools")
     ap.add_argument("--comix", action="store_true",
                     help="instead of the decode job: time the CoMixKV controller (sensitivity kernel + allocation) "
                          "on the Qwen3-32B shape and measure the attention error of its bits against uniform 3 bits")
@@ -132,6 +136,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "qwen3_32b_comix":
+        qwen_bench(args)
+        return
     import torch
 
     import workloads as wl
@@ -310,6 +317,110 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, steps_per_job)
     print(json.dumps(line), flush=True)
+
+
+def qwen_bench(args):
+    """The Qwen3-32B CoMixKV workload: 8 agents, each with its own pool of 8064 tokens
+    (64 layers, 8 kv heads, d 128, V bits per layer a seeded permutation of 21 x 2, 22 x 3,
+    21 x 4) and a fixed 128-token native window; 64 query heads.  One step = one job: the
+    8 pools encoded from bf16 K/V already in HBM, then 16 decode calls for the 8 agents.
+    K, V = N(0, 1) * sigma with sigma ~ LogNormal(0, 0.5) per (layer, kv head, channel), drawn
+    on the device (the workload's own recipe; its host slices are used by the parity tests).
+    """
+    import torch
+
+    import workloads as wl
+    from quantized_shared_kv_amd import polykv as pk
+
+    pk.lib()
+    w = wl.QWEN3_32B_MIXED
+    dev = "cuda:0"
+    L, Hkv, Hq, d, T, A, S = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens, w.n_agents, w.sfx_tokens
+    NS = args.decode_steps or w.steps
+    t0 = time.time()
+    log("[bench] generating inputs (device draws)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    kv = []
+    for p in range(A):
+        sk = torch.exp(0.5 * torch.randn((L, Hkv, 1, d), generator=g, device=dev))
+        sv = torch.exp(0.5 * torch.randn((L, Hkv, 1, d), generator=g, device=dev))
+        k = torch.empty((L, Hkv, T, d), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        for l in range(L):
+            k[l] = (torch.randn((Hkv, T, d), generator=g, device=dev) * sk[l]).to(torch.bfloat16)
+            v[l] = (torch.randn((Hkv, T, d), generator=g, device=dev) * sv[l]).to(torch.bfloat16)
+        kv.append((k, v))
+    sfx_k = torch.randn((A, L, Hkv, S, d), generator=g, device=dev).to(torch.bfloat16)
+    sfx_v = torch.randn((A, L, Hkv, S, d), generator=g, device=dev).to(torch.bfloat16)
+    q_all = torch.randn((NS, A, L, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((A, L, Hq, d), dtype=torch.float32, device=dev)
+    cfgs = [pk.make_config(L, Hkv, d, T, w.v_bits(p)) for p in range(A)]
+    bufs = [torch.empty(pk.pool_bytes(c), dtype=torch.uint8, device=dev) for c in cfgs]
+    pools = [pk.pool_build(c, b.data_ptr(), b.numel()) for c, b in zip(cfgs, bufs)]
+    for p in range(A):
+        pk.pool_quantize_append(pools[p], 0, *kv[p])
+    ws = torch.empty(pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in {time.time() - t0:.1f}s; pools {sum(b.numel() for b in bufs) / 1e9:.2f} GB")
+    EV_EVERY = 4
+    timed_calls = list(range(0, NS, EV_EVERY))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(NS)]
+    for e0, e1 in evs:
+        e0.record()
+        e1.record()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def one_job(timed):
+        for p in range(A):
+            fresh = pk.pool_build(cfgs[p], bufs[p].data_ptr(), bufs[p].numel())  # host-only: n_tokens back to 0
+            for f in pk.Pool._fields_:
+                setattr(pools[p], f[0], getattr(fresh, f[0]))
+        if timed:
+            b0.record()
+        for p in range(A):
+            pk.pool_quantize_append(pools[p], 0, *kv[p])
+        if timed:
+            b1.record()
+        for s in range(NS):
+            pk.agent_decode_attention(pools, q_all[s], out, 0, sfx_k, sfx_v, [S] * A, workspace=ws,
+                                      pool_events=evs[s] if timed and s % EV_EVERY == 0 else None)
+
+    for i in range(args.warmup):
+        one_job(False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pool_ms, build_ms = [], []
+    start.record()
+    for i in range(args.steps):
+        one_job(True)
+        torch.cuda.synchronize()
+        pool_ms += [evs[s][0].elapsed_time(evs[s][1]) for s in timed_calls]
+        build_ms.append(b0.elapsed_time(b1))
+        log(f"[bench] step {i + 1}/{args.steps} done")
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    pool_alg = sum(T * (Hkv * (d + d * int(b) // 8 + 4) + 4) for p in range(A) for b in w.v_bits(p))
+    alg = pool_alg + A * L * Hq * d * 2 + A * L * Hq * d * 4
+    avg = float(np.mean(pool_ms))
+    achieved = alg / (avg / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "compressed-KV decode attention: achieved HBM GB/s (% peak) + agent-tokens/s",
+        "value": A * NS / (ms_per_step / 1e3), "unit": "agent-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32-acc", "data": "synthetic",
+        "config": {"workload": w.name, "agents": A, "pools": A, "decode_steps_per_step": NS, "pool_tokens": T,
+                   "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "v_bits": "per (pool, layer): seeded permutation of 21x2, 22x3, 21x4",
+                   "suffix": f"bf16, {S} tokens per agent"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "pool decode",
+                     "alg_bytes_per_launch": alg, "avg_launch_us": avg * 1e3, "launches_timed": len(pool_ms)},
+        "pool_build_us": float(np.mean(build_ms)) * 1e3,
+        "decode_step_us": (ms_per_step - float(np.mean(build_ms))) / NS * 1e3,
+    }), flush=True)
 
 
 def comix_bench():
