@@ -196,6 +196,48 @@ typedef struct {
 int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
                            void* stream);
 
+/* ---- handing a pool over, and kv-head shards ---- */
+
+/* Header of a pool image handed to another buffer, process or device: with the
+ * image bytes (pool->bytes bytes from pool->base, position-independent) it
+ * recreates the pool (PolyKV explainer, section 2.A: the shared context is one
+ * compressed object that every agent reads).  Plain host data. */
+typedef struct {
+    uint32_t magic;                      /* 0x31564B50 ("PKV1") */
+    int32_t abi_version;                 /* pkv_version() of the writer; the major part must match */
+    pkv_pool_config cfg;
+    int32_t n_tokens[PKV_MAX_LAYERS];    /* tokens stored per layer */
+    uint64_t image_bytes;                /* = pool_bytes(&cfg) */
+} pkv_pool_header;
+
+/* Fill *out from a pool's descriptor.  Host only.  Errors: PKV_EINVAL. */
+int pool_export_header(const pkv_pool* pool, pkv_pool_header* out);
+
+/*
+ * Describe an image whose bytes the caller has already placed at dev_buf
+ * (device, 256-byte aligned, dev_bytes >= hdr->image_bytes): writes *out like
+ * pool_build, with the header's token counts.  Host only, nothing enqueued.
+ * Errors: PKV_EINVAL (magic, version, size or token counts inconsistent),
+ * PKV_EUNSUPPORTED, PKV_ENOSPACE.
+ */
+int pool_import(const pkv_pool_header* hdr, void* dev_buf, size_t dev_bytes, pkv_pool* out);
+
+/*
+ * A pool holding kv heads [head_begin, head_begin + head_count) of src, laid
+ * out in dev_buf (256-byte aligned, not overlapping src's buffer, dev_bytes >=
+ * pool_bytes of src's config with n_kv_heads = head_count): per layer the K
+ * codes, V norms, V maxima and V codes of those heads and all K scales are
+ * copied (device to device, enqueued on stream); *out gets src's token counts.
+ * Decoding the shard with query heads [head_begin * G, (head_begin +
+ * head_count) * G) of each agent gives the outputs the whole pool gives for
+ * those heads (each (layer, kv head) is decoded independently), which is how
+ * a pool splits over devices.  Later appends to the shard take their K scale
+ * over the shard's heads only.
+ * Errors: PKV_EINVAL, PKV_ENOSPACE, PKV_EHIP (a copy could not be enqueued).
+ */
+int pool_shard(const pkv_pool* src, int32_t head_begin, int32_t head_count, void* dev_buf, size_t dev_bytes,
+               pkv_pool* out, void* stream);
+
 /* ---- CoMixKV controller: sensitivity and joint bit allocation ---- */
 
 /* Arguments of one sensitivity estimate (CoMixKV news article, abstract and
@@ -262,7 +304,8 @@ const char* pkv_strerror(int code);
 int pkv_version(void);
 
 /* sizeof of the ABI structs, for bindings to check their mirrors:
- * which = 0: pkv_pool_config, 1: pkv_pool, 2: pkv_decode_args, 3: pkv_comix_args; else 0. */
+ * which = 0: pkv_pool_config, 1: pkv_pool, 2: pkv_decode_args, 3: pkv_comix_args,
+ * 4: pkv_pool_header; else 0. */
 size_t pkv_abi_sizeof(int32_t which);
 
 /*

@@ -16,6 +16,12 @@ order, each starting on a 256-byte boundary:
   Vc    u8    per layer l: [Hkv][tc/8][d * b_l]   packed V code groups
   amax  u32   [L]                     scratch of the quantiser (not part of the image)
 
+A kv-head shard (``PoolImage.shard``) is the same pool restricted to a range
+of kv heads: the per-head regions keep only those heads, the K scales (one per
+token, shared by the heads) stay whole, and the token counts are unchanged.
+This is the layout-level definition the device copy must reproduce; each
+(layer, kv head) decodes exactly as in the whole pool.
+
 A later append writes new tokens after the existing ones and never rewrites
 the codes, norms or scales of earlier tokens (CoMixKV news article,
 "incremental quantization strategy": quantised blocks are not re-quantised);
@@ -140,3 +146,18 @@ class PoolImage:
         khat = self.ks[layer, :t, None].astype(np.float64) * self.kq[layer, kv_head, :t].astype(np.float64)
         vhat = codec.v_decode(self.vn[layer, kv_head, :t], self.codes[layer, kv_head, :t], self.lay.bits[layer])
         return khat, vhat
+
+    def shard(self, head_begin: int, head_count: int) -> "PoolImage":
+        """The pool restricted to kv heads [head_begin, head_begin + head_count)."""
+        lay = self.lay
+        if head_begin < 0 or head_count < 1 or head_begin + head_count > lay.n_kv_heads:
+            raise ValueError("head range")
+        out = PoolImage(lay.n_layers, head_count, lay.head_dim, lay.capacity, lay.bits)
+        sl = slice(head_begin, head_begin + head_count)
+        out.n_tokens = self.n_tokens.copy()
+        out.kq = self.kq[:, sl].copy()
+        out.vn = self.vn[:, sl].copy()
+        out.ks = self.ks.copy()
+        out.vmax = self.vmax[:, sl].copy()
+        out.codes = self.codes[:, sl].copy()
+        return out

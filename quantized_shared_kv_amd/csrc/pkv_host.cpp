@@ -156,7 +156,7 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 102; }
+int pkv_version(void) { return 103; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {
@@ -164,6 +164,7 @@ size_t pkv_abi_sizeof(int32_t which) {
         case 1: return sizeof(pkv_pool);
         case 2: return sizeof(pkv_decode_args);
         case 3: return sizeof(pkv_comix_args);
+        case 4: return sizeof(pkv_pool_header);
         default: return 0;
     }
 }

@@ -14,7 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
-ABI_VERSION = 102  # pkv_version() of the library these ctypes mirrors describe
+ABI_VERSION = 103  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -56,6 +56,11 @@ class ComixArgs(ctypes.Structure):
                 ("win_cap", c_int32), ("win_len", POINTER(c_int32)), ("out", c_void_p)]
 
 
+class PoolHeader(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("abi_version", c_int32), ("cfg", PoolConfig),
+                ("n_tokens", c_int32 * MAX_LAYERS), ("image_bytes", c_uint64)]
+
+
 _LIB = None
 
 
@@ -82,6 +87,12 @@ def lib() -> ctypes.CDLL:
         L.pkv_abi_sizeof.restype = c_size_t
         L.pkv_lloyd_max_table.argtypes = [c_int32, POINTER(c_float), POINTER(c_float)]
         L.pkv_lloyd_max_table.restype = c_int32
+        L.pool_export_header.argtypes = [POINTER(Pool), POINTER(PoolHeader)]
+        L.pool_export_header.restype = c_int32
+        L.pool_import.argtypes = [POINTER(PoolHeader), c_void_p, c_size_t, POINTER(Pool)]
+        L.pool_import.restype = c_int32
+        L.pool_shard.argtypes = [POINTER(Pool), c_int32, c_int32, c_void_p, c_size_t, POINTER(Pool), c_void_p]
+        L.pool_shard.restype = c_int32
         L.pkv_lloyd_max_distortion.argtypes = [c_int32]
         L.pkv_lloyd_max_distortion.restype = ctypes.c_double
         L.comix_sensitivity.argtypes = [POINTER(ComixArgs), c_void_p]
@@ -89,7 +100,7 @@ def lib() -> ctypes.CDLL:
         L.comix_allocate_bits.argtypes = [c_int32, POINTER(c_float), POINTER(c_uint64), POINTER(ctypes.c_double),
                                           c_uint64, POINTER(c_uint8)]
         L.comix_allocate_bits.restype = c_int32
-        for i, s in enumerate((PoolConfig, Pool, DecodeArgs, ComixArgs)):
+        for i, s in enumerate((PoolConfig, Pool, DecodeArgs, ComixArgs, PoolHeader)):
             if L.pkv_abi_sizeof(i) != ctypes.sizeof(s):
                 raise ImportError(f"ABI mismatch for {s.__name__}")
         if L.pkv_version() != ABI_VERSION:
@@ -261,3 +272,25 @@ def comix_allocate_bits(sensitivity, cost, error_factor, budget: int):
     out = (c_uint8 * max(n, 1))()
     _check(lib().comix_allocate_bits(n, s, c, e, int(budget), out), "comix_allocate_bits")
     return [int(out[i]) for i in range(n)]
+
+
+def pool_export_header(pool) -> PoolHeader:
+    """The handoff header of a pool (host only)."""
+    h = PoolHeader()
+    _check(lib().pool_export_header(ctypes.byref(pool), ctypes.byref(h)), "pool_export_header")
+    return h
+
+
+def pool_import(header, dev_ptr: int, dev_bytes: int):
+    """Describe an image already copied to dev_ptr (host only)."""
+    p = Pool()
+    _check(lib().pool_import(ctypes.byref(header), c_void_p(dev_ptr), dev_bytes, ctypes.byref(p)), "pool_import")
+    return p
+
+
+def pool_shard(src, head_begin: int, head_count: int, dev_ptr: int, dev_bytes: int, stream=None):
+    """A pool of kv heads [head_begin, head_begin + head_count) of src in the given device buffer."""
+    p = Pool()
+    _check(lib().pool_shard(ctypes.byref(src), head_begin, head_count, c_void_p(dev_ptr), dev_bytes, ctypes.byref(p),
+                            c_void_p(_stream_handle(stream))), "pool_shard")
+    return p

@@ -28,7 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"pool_bytes", "pool_build", "pool_quantize_append", "agent_decode_attention",
-                          "comix_sensitivity", "comix_allocate_bits", "pkv_lloyd_max_distortion"}
+                          "comix_sensitivity", "comix_allocate_bits", "pkv_lloyd_max_distortion",
+                          "pool_export_header", "pool_import", "pool_shard"}
     lib = pk.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -40,7 +41,8 @@ def test_struct_mirrors_match_c_sizes():
     assert lib.pkv_abi_sizeof(1) == ctypes.sizeof(pk.Pool)
     assert lib.pkv_abi_sizeof(2) == ctypes.sizeof(pk.DecodeArgs)
     assert lib.pkv_abi_sizeof(3) == ctypes.sizeof(pk.ComixArgs)
-    assert lib.pkv_abi_sizeof(4) == 0
+    assert lib.pkv_abi_sizeof(4) == ctypes.sizeof(pk.PoolHeader)
+    assert lib.pkv_abi_sizeof(5) == 0
     assert lib.pkv_version() == pk.ABI_VERSION
 
 

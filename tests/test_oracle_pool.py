@@ -111,3 +111,29 @@ def test_image_bytes_place_every_region():
     vc1 = buf[lay.vc[1]:lay.vc[2]].reshape(1, lay.tc // 8, 64 * 4)
     assert np.array_equal(vc1, img.packed_codes(1))
     assert not buf[lay.amax:].any()
+
+
+def test_shard_decodes_like_the_whole_pool_and_tiles_it():
+    """A kv-head shard decodes each of its heads exactly as the whole pool does, and the
+    shards of a partition of the heads hold exactly the whole pool's per-head data."""
+    rng = np.random.default_rng(5)
+    L, H, d, T = 3, 4, 64, 70
+    img = pool_image.PoolImage(L, H, d, 96, [2, 3, 4])
+    img.append(0, rng.standard_normal((L, H, T, d)), rng.standard_normal((L, H, T, d)))
+    assert np.array_equal(img.shard(0, H).image(), img.image())
+    parts = [(0, 1), (1, 2), (3, 1)]
+    shards = [img.shard(h0, hc) for h0, hc in parts]
+    for (h0, hc), sh in zip(parts, shards):
+        assert sh.lay.total == pool_image.layout(L, hc, d, 96, [2, 3, 4]).total
+        for l in range(L):
+            for g in range(hc):
+                kf, vf = img.decoded_layer(l, h0 + g)
+                ks_, vs_ = sh.decoded_layer(l, g)
+                assert np.array_equal(kf, ks_) and np.array_equal(vf, vs_)
+    assert np.array_equal(np.concatenate([s.kq for s in shards], axis=1), img.kq)
+    assert np.array_equal(np.concatenate([s.codes for s in shards], axis=1), img.codes)
+    assert np.array_equal(np.concatenate([s.vmax for s in shards], axis=1), img.vmax)
+    for s in shards:
+        assert np.array_equal(s.ks, img.ks)
+    with pytest.raises(ValueError):
+        img.shard(3, 2)
