@@ -19,6 +19,12 @@ PolyKV explainer, section 2.B (asymmetric compression scheme):
   v_hat = (n / d) * H @ c[code], exact in fp64.
 * CoMixKV news article ("incremental quantization strategy"; abstract): the V
   bit width is 2, 3 or 4 per (agent, layer); K stays int8.
+* Randomised rotation (a codec variant measured as an ablation; the pages name
+  only the plain FWHT): with a sign vector s in {+1, -1}^d, the rotation is H D
+  (D = diag(s)): x is multiplied by s before the transform, and the decoded
+  vector by s after the inverse transform, v_hat = s * (n / d) H c[code].  The
+  norm is unchanged (squares do not see signs), and s = all +1 is the plain
+  codec.  The signs are an input (chosen by the caller), not drawn here.
 
 Code-group packing (the layout the decode kernels read).  Tokens of one
 (layer, kv head) are packed in groups of 8 consecutive tokens.  A group of
@@ -58,11 +64,16 @@ def k_dequantize(scale, q: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- V codec
-def v_encode(v: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
-    """Encode V vectors (last axis = head_dim) to (norms fp32, codes uint8)."""
+def v_encode(v: np.ndarray, bits: int, signs: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Encode V vectors (last axis = head_dim) to (norms fp32, codes uint8).
+
+    signs: optional [d] array of +1 / -1 applied to each vector before the FWHT.
+    """
     x = np.asarray(v, dtype=np.float32)
     _, thr = lloyd_max.table_f32(bits)
     n = hadamard.norm_f32(x)
+    if signs is not None:
+        x = x * np.asarray(signs, dtype=np.float32)  # exact: sign flips
     z = hadamard.fwht_f32(x)
     nz = n > 0
     r = np.zeros_like(n)
@@ -75,13 +86,22 @@ def v_encode(v: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
     return n, codes
 
 
-def v_decode(norm: np.ndarray, codes: np.ndarray, bits: int) -> np.ndarray:
-    """v_hat = (n / d) * H @ c[code] in fp64 (inverse FWHT of the centroid vector)."""
+def v_decode(norm: np.ndarray, codes: np.ndarray, bits: int, signs: np.ndarray | None = None) -> np.ndarray:
+    """v_hat = s * (n / d) * H @ c[code] in fp64 (inverse FWHT of the centroid vector)."""
     cent, _ = lloyd_max.table_f32(bits)
     c = cent.astype(np.float64)[np.asarray(codes, dtype=np.int64)]
     d = c.shape[-1]
     h = hadamard.hadamard_matrix(d).astype(np.float64)
-    return (np.asarray(norm, dtype=np.float64)[..., None] / d) * (c @ h)
+    out = (np.asarray(norm, dtype=np.float64)[..., None] / d) * (c @ h)
+    if signs is not None:
+        out = out * np.asarray(signs, dtype=np.float64)
+    return out
+
+
+def signs_from_mask(mask: bytes | np.ndarray, d: int) -> np.ndarray:
+    """[d] +1 / -1 from a little-endian bit mask (bit i set: dimension i negated)."""
+    b = np.unpackbits(np.frombuffer(bytes(mask), dtype=np.uint8), bitorder="little")[:d]
+    return np.where(b == 1, -1.0, 1.0)
 
 
 # ---------------------------------------------------------------- packing

@@ -93,7 +93,9 @@ def bf16_kv_bytes(n_layers: int, n_kv_heads: int, head_dim: int, tokens: int) ->
 class PoolImage:
     """Host model of one pool: encodes appends and writes the image bytes."""
 
-    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits):
+    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits, signs=None):
+        """signs: optional [head_dim] +1 / -1 of the randomised rotation (None: plain FWHT)."""
+        self.signs = None if signs is None else np.asarray(signs, dtype=np.float64)
         self.lay = layout(n_layers, n_kv_heads, head_dim, capacity, bits)
         L, H, d, tc = n_layers, n_kv_heads, head_dim, self.lay.tc
         self.n_tokens = np.zeros(L, dtype=np.int64)
@@ -116,7 +118,7 @@ class PoolImage:
             s, q = codec.k_quantize(k[j])
             self.kq[l, :, t0:t0 + n] = q
             self.ks[l, t0:t0 + n] = s
-            nrm, codes = codec.v_encode(v[j], self.lay.bits[l])
+            nrm, codes = codec.v_encode(v[j], self.lay.bits[l], self.signs)
             self.vn[l, :, t0:t0 + n] = nrm
             if n:
                 self.vmax[l] = np.maximum(self.vmax[l], nrm.max(axis=1))
@@ -144,7 +146,8 @@ class PoolImage:
         """(K_hat, V_hat) [T][d] in fp64 for the tokens in the pool."""
         t = int(self.n_tokens[layer])
         khat = self.ks[layer, :t, None].astype(np.float64) * self.kq[layer, kv_head, :t].astype(np.float64)
-        vhat = codec.v_decode(self.vn[layer, kv_head, :t], self.codes[layer, kv_head, :t], self.lay.bits[layer])
+        vhat = codec.v_decode(self.vn[layer, kv_head, :t], self.codes[layer, kv_head, :t], self.lay.bits[layer],
+                              self.signs)
         return khat, vhat
 
     def shard(self, head_begin: int, head_count: int) -> "PoolImage":
@@ -152,7 +155,7 @@ class PoolImage:
         lay = self.lay
         if head_begin < 0 or head_count < 1 or head_begin + head_count > lay.n_kv_heads:
             raise ValueError("head range")
-        out = PoolImage(lay.n_layers, head_count, lay.head_dim, lay.capacity, lay.bits)
+        out = PoolImage(lay.n_layers, head_count, lay.head_dim, lay.capacity, lay.bits, self.signs)
         sl = slice(head_begin, head_begin + head_count)
         out.n_tokens = self.n_tokens.copy()
         out.kq = self.kq[:, sl].copy()

@@ -147,3 +147,62 @@ def test_pack_roundtrip_and_vectorised_agrees(bits, d):
     for a in range(3):
         for g in range(5):
             assert np.array_equal(packed[a, g], codec.pack_group(codes[a, 8 * g:8 * g + 8], bits))
+
+
+# ---- randomised rotation (sign vector before the FWHT), a codec variant
+@pytest.mark.parametrize("d", [64, 128])
+def test_signed_rotation_is_orthogonal_and_plain_when_all_positive(d):
+    rng = np.random.default_rng(d)
+    s = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    h = hadamard.hadamard_matrix(d).astype(np.float64)
+    t = h @ np.diag(s)
+    assert np.array_equal(t.T @ t, d * np.eye(d))
+    v = rng.standard_normal((20, d)).astype(np.float32)
+    n0, c0 = codec.v_encode(v, 3)
+    n1, c1 = codec.v_encode(v, 3, np.ones(d))
+    assert np.array_equal(n0, n1) and np.array_equal(c0, c1)
+    assert np.array_equal(codec.v_decode(n0, c0, 3), codec.v_decode(n1, c1, 3, np.ones(d)))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_all_negative_signs_mirror_the_codes(bits):
+    """Negating every coordinate negates y, and the symmetric table maps code c to 2^b - 1 - c."""
+    rng = np.random.default_rng(bits)
+    v = rng.standard_normal((50, 64)).astype(np.float32)
+    n0, c0 = codec.v_encode(v, bits)
+    n1, c1 = codec.v_encode(v, bits, -np.ones(64))
+    assert np.array_equal(n0, n1)
+    # except where y lies exactly on a threshold (a tie takes the lower code on both sides);
+    # here that is y == 0, which the transform of -v also gives as +0.0
+    y = hadamard.fwht_f32(v) * (np.float32(1) / n0)[:, None]
+    _, thr = lloyd_max.table_f32(bits)
+    tie = np.isin(y, thr)
+    assert np.array_equal(c1.astype(int)[~tie], ((1 << bits) - 1 - c0.astype(int))[~tie])
+    assert np.array_equal(c1[tie], c0[tie])
+    np.testing.assert_allclose(codec.v_decode(n1, c1, bits, -np.ones(64)), codec.v_decode(n0, c0, bits), rtol=0,
+                               atol=1e-12)
+
+
+def test_signed_rotation_fixes_hadamard_aligned_vectors():
+    """A vector along a Hadamard row becomes one spike under the plain FWHT (the codec clips it);
+    random signs spread it, so the error returns to the Lloyd-Max level."""
+    d, bits = 128, 3
+    rng = np.random.default_rng(9)
+    h = hadamard.hadamard_matrix(d).astype(np.float32)
+    v = h[rng.integers(0, d, 64)] * rng.lognormal(0.0, 1.0, (64, 1)).astype(np.float32)
+    s = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+
+    def rel_mse(signs):
+        n, c = codec.v_encode(v, bits, signs)
+        vh = codec.v_decode(n, c, bits, signs)
+        return float(np.mean(np.sum((vh - v) ** 2, axis=1) / np.sum(v.astype(np.float64) ** 2, axis=1)))
+
+    plain, signed = rel_mse(None), rel_mse(s)
+    assert plain > 0.5                      # the spike at sqrt(d) = 11.3 is clipped to 2.15
+    assert signed < 2.0 * 0.03455           # near D_3 for 3 bits
+
+
+def test_signs_from_mask_bit_order():
+    m = bytes([0b00000101] + [0] * 15)
+    s = codec.signs_from_mask(m, 128)
+    assert s[0] == -1 and s[1] == 1 and s[2] == -1 and np.all(s[3:] == 1)
