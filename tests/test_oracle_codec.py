@@ -179,8 +179,9 @@ def test_all_negative_signs_mirror_the_codes(bits):
     tie = np.isin(y, thr)
     assert np.array_equal(c1.astype(int)[~tie], ((1 << bits) - 1 - c0.astype(int))[~tie])
     assert np.array_equal(c1[tie], c0[tie])
-    np.testing.assert_allclose(codec.v_decode(n1, c1, bits, -np.ones(64)), codec.v_decode(n0, c0, bits), rtol=0,
-                               atol=1e-12)
+    rows = ~tie.any(axis=1)  # vectors without a tie decode to the same values
+    np.testing.assert_allclose(codec.v_decode(n1, c1, bits, -np.ones(64))[rows], codec.v_decode(n0, c0, bits)[rows],
+                               rtol=0, atol=1e-12)
 
 
 def test_signed_rotation_fixes_hadamard_aligned_vectors():
