@@ -49,13 +49,19 @@ enum {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
-/* Shape of one pool.  K always uses 8 bits; V uses v_bits[l] bits in layer l. */
+/* Shape of one pool.  K always uses 8 bits; V uses v_bits[l] bits in layer l.
+ * v_signs: the V rotation's sign mask, bit i (little-endian over the 16 bytes)
+ * set = coordinate i of every V vector negated before the FWHT and the decoded
+ * output negated after the inverse FWHT (rotation H D with D = diag(+-1), a
+ * randomised-Hadamard variant chosen by the caller); all zero = the plain FWHT
+ * of PolyKV explainer, section 2.B.  Bits at or above head_dim must be 0. */
 typedef struct {
     int32_t n_layers;                /* 1 .. PKV_MAX_LAYERS */
     int32_t n_kv_heads;              /* >= 1 */
     int32_t head_dim;                /* 64 or 128 */
     int32_t capacity_tokens;         /* >= 1; rounded up to a multiple of 32 internally */
     uint8_t v_bits[PKV_MAX_LAYERS];  /* 2, 3 or 4 for layers 0 .. n_layers-1 */
+    uint8_t v_signs[16];             /* rotation sign mask (see above); zero = plain FWHT */
 } pkv_pool_config;
 
 /*
@@ -159,7 +165,8 @@ typedef struct {
                                       /* optional, host [n_agents]: NULL, or per agent NULL or a second
                                          pool the agent alone (or every agent naming it) also attends:
                                          its own older tokens, quantized once when they left the
-                                         native window (pool_quantize_append on that pool) */
+                                         native window (pool_quantize_append on that pool); it must
+                                         use the same v_signs as the agent's shared pool */
 } pkv_decode_args;
 
 #define PKV_KERNEL_DEFAULT 0

@@ -29,6 +29,7 @@ struct PoolEntry {
                            // its first unit there; -1: decoded by the pool kernel
     int32_t agent_base;    // >= 0: the pool's launch agents agent0 + i are call agents
                            // agent_base + i (no table lookup needed); -1 otherwise
+    uint32_t vsign[4];     // V rotation sign mask: output dimension i negated after the inverse FWHT
 };
 
 struct DecodeLaunch {

@@ -1074,7 +1074,7 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
             }
         }
     }
-    // inverse transform: H z / D (lane holds dims EPL*lane + e)
+    // inverse transform: H z / D (lane holds dims EPL*lane + e), then the rotation's signs
     if (EPL == 2) {
         const float u = z[0], w = z[EPL - 1];
         z[0] = u + w;
@@ -1088,6 +1088,13 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
             const float pz = __shfl_xor(z[e], off, 64);
             z[e] = upper ? (pz - z[e]) : (z[e] + pz);
         }
+    }
+    {
+        const uint32_t* vs = a.pools[a.agent_pool[k]].vsign;
+        const int d0 = EPL * lane;
+        const uint32_t sb = (vs[d0 >> 5] >> (d0 & 31)) & ((1u << EPL) - 1u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) z[e] = __uint_as_float(__float_as_uint(z[e]) ^ (((sb >> e) & 1u) << 31));
     }
     const float inv_d = 1.0f / D;
     float o[EPL];
@@ -1199,6 +1206,7 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.off_ks = p->off_ks;
             e.off_vmax = p->off_vmax;
             e.off_vc0 = p->off_vc[0];
+            std::memcpy(e.vsign, p->cfg.v_signs, sizeof(e.vsign));
             for (int l = 0; l < p->cfg.n_layers; ++l) {
                 if (p->cfg.v_bits[l] >= 3) e.ge3[l >> 5] |= 1u << (l & 31);
                 if (p->cfg.v_bits[l] == 4) e.eq4[l >> 5] |= 1u << (l & 31);
@@ -1326,6 +1334,9 @@ int validate(const pkv_decode_args* x) {
             // a private pool is attended in addition to the shared one, never instead of it
             for (int b = 0; b < x->n_agents; ++b)
                 if (x->agent_pool[b] == p) return PKV_EINVAL;
+            // their rotated-domain sums are added before one inverse transform: same rotation
+            if (std::memcmp(p->cfg.v_signs, x->agent_pool[a]->cfg.v_signs, sizeof(p->cfg.v_signs)) != 0)
+                return PKV_EINVAL;
         }
     }
     if (x->n_q_heads % p0->cfg.n_kv_heads) return PKV_EINVAL;

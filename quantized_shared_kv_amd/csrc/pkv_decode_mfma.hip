@@ -937,6 +937,12 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         stage(std::integral_constant<int, 2>{});
         stage(std::integral_constant<int, 4>{});
         stage(std::integral_constant<int, 8>{});
+        {  // the rotation's signs: output dimension FD * fl + e negated where its bit is set
+            const int d0 = FD * fl;
+            const uint32_t sb = (P.vsign[d0 >> 5] >> (d0 & 31)) & ((1u << FD) - 1u);
+#pragma unroll
+            for (int e = 0; e < FD; ++e) z[e] = __uint_as_float(__float_as_uint(z[e]) ^ (((sb >> e) & 1u) << 31));
+        }
         const float mu = su_m[i];
         const float M2 = fmaxf(M, mu);
         const float ap = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - M2);

@@ -87,6 +87,9 @@ bool config_valid(const pkv_pool_config* cfg, int* err) {
     if (cfg->head_dim != 64 && cfg->head_dim != 128) return false;
     for (int l = 0; l < cfg->n_layers; ++l)
         if (cfg->v_bits[l] < 2 || cfg->v_bits[l] > 4) return false;
+    *err = PKV_EINVAL;
+    for (int i = cfg->head_dim / 8; i < 16; ++i)
+        if (cfg->v_signs[i]) return false;  // sign bits past head_dim
     // keep every region offset inside 64-bit arithmetic with a wide margin
     const double est = (double)cfg->n_layers * cfg->n_kv_heads * ((double)cfg->capacity_tokens + 32) *
                        (cfg->head_dim * 1.5 + 8.0);
@@ -156,7 +159,7 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 103; }
+int pkv_version(void) { return 104; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {

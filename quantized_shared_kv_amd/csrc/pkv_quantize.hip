@@ -41,6 +41,7 @@ struct EncodeArgs {
     int32_t l0, nl;
     uint8_t bits[kMaxLayersArg];     // bits of each call layer
     float thr[3][15];
+    uint32_t vsign[4];               // V rotation sign mask: bit i set = coordinate i negated
 };
 
 __device__ __forceinline__ float load_elem(const void* p, int dtype, uint64_t i) {
@@ -316,7 +317,19 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
         nrm[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(n_l), i));
         rcp[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_l), i));
     }
-    // ---- FWHT, ascending half-width (the in-lane stage first when EPL == 2)
+    // ---- the rotation's signs (coordinate EPL * lane + e negated where its mask bit is set;
+    // the norm above does not see them), then the FWHT, ascending half-width (the in-lane
+    // stage first when EPL == 2)
+    {
+        const int d0 = EPL * lane;
+        const uint32_t sb = (a.vsign[d0 >> 5] >> (d0 & 31)) & ((1u << EPL) - 1u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const uint32_t flip = ((sb >> e) & 1u) << 31;
+#pragma unroll
+            for (int i = 0; i < kGroupTokens; ++i) vx[i][e] = __uint_as_float(__float_as_uint(vx[i][e]) ^ flip);
+        }
+    }
     if (EPL == 2) {
 #pragma unroll
         for (int i = 0; i < kGroupTokens; ++i) {
@@ -471,6 +484,7 @@ extern "C" int pool_quantize_append(pkv_pool* pool, int32_t layer_begin, int32_t
     a.l0 = layer_begin;
     a.nl = layer_count;
     std::memcpy(a.thr, codebook_tables().thr, sizeof(a.thr));
+    std::memcpy(a.vsign, c.v_signs, sizeof(a.vsign));
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(k_reset, dim3(layer_count), dim3(64), 0, s, a);

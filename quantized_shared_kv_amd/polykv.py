@@ -14,7 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
-ABI_VERSION = 103  # pkv_version() of the library these ctypes mirrors describe
+ABI_VERSION = 104  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -30,7 +30,7 @@ class PolyKVError(RuntimeError):
 
 class PoolConfig(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
-                ("capacity_tokens", c_int32), ("v_bits", c_uint8 * MAX_LAYERS)]
+                ("capacity_tokens", c_int32), ("v_bits", c_uint8 * MAX_LAYERS), ("v_signs", c_uint8 * 16)]
 
 
 class Pool(ctypes.Structure):
@@ -132,11 +132,20 @@ def _stream_handle(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream)
 
 
-def make_config(n_layers: int, n_kv_heads: int, head_dim: int, capacity_tokens: int, v_bits) -> PoolConfig:
+def make_config(n_layers: int, n_kv_heads: int, head_dim: int, capacity_tokens: int, v_bits,
+                v_signs=None) -> PoolConfig:
+    """v_signs: optional head_dim values, negative (or True) where the V rotation negates a coordinate."""
     cfg = PoolConfig(n_layers, n_kv_heads, head_dim, capacity_tokens)
     vb = list(v_bits) if hasattr(v_bits, "__len__") else [int(v_bits)] * n_layers
     for i, b in enumerate(vb):
         cfg.v_bits[i] = int(b)
+    if v_signs is not None:
+        neg = [bool(x < 0) if not isinstance(x, bool) else x for x in v_signs]
+        if len(neg) != head_dim:
+            raise ValueError("one sign per head dimension")
+        for i, n in enumerate(neg):
+            if n:
+                cfg.v_signs[i // 8] |= 1 << (i % 8)
     return cfg
 
 

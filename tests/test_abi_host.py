@@ -230,3 +230,23 @@ def test_decode_private_pools_workspace_and_errors():
         pk.agent_decode_attention([pool] * A, q, out, private_pools=[pool, None, None])
     with pytest.raises(ValueError):  # one entry per agent
         pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv])
+    prv.cfg.v_signs[0] = 1
+    with pytest.raises(pk.PolyKVError):  # a different V rotation from the shared pool's
+        pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv, None, None])
+    pool.cfg.v_signs[0] = 1  # the same rotation on both
+    pk.agent_decode_attention([pool] * A, q, out, private_pools=[prv, None, None])
+
+
+def test_rotation_signs_in_the_config():
+    import workloads as wl
+
+    s = wl.rotation_signs(0, 64)
+    cfg = pk.make_config(2, 2, 64, 40, [3, 3], v_signs=s)
+    mask = bytes(cfg.v_signs)
+    assert all(mask[i] == 0 for i in range(8, 16))
+    assert [(mask[i // 8] >> (i % 8)) & 1 for i in range(64)] == [int(x < 0) for x in s]
+    assert pk.pool_bytes(cfg) == pk.pool_bytes(pk.make_config(2, 2, 64, 40, [3, 3]))  # same layout
+    cfg.v_signs[8] = 1  # a sign past head_dim 64
+    assert pk.pool_bytes(cfg) == 0
+    with pytest.raises(ValueError):
+        pk.make_config(2, 2, 64, 40, [3, 3], v_signs=s[:10])

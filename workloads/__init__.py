@@ -42,7 +42,13 @@ TENSOR_IDS = {
     "sfx_v": 5,
     "q_steps": 6,
     "v_bits": 7,
+    "v_signs": 8,
 }
+
+
+def rotation_signs(seed: int, head_dim: int, key: int = 0) -> np.ndarray:
+    """[head_dim] +1 / -1 (each with probability 1/2): the sign vector of a randomised V rotation."""
+    return np.where(rng_for(seed, "v_signs", key).random(head_dim) < 0.5, -1.0, 1.0)
 
 
 def rng_for(seed: int, tensor: str, *key: int) -> np.random.Generator:
