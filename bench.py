@@ -15,6 +15,7 @@ same work.  Only the ``cpu_baseline`` leg imports the oracle.
     python bench.py [--steps K] [--warmup W] [--kernel valu|mfma|default] [--no-cpu-baseline]
     python bench.py --workload qwen3_32b_comix   (8 agents, own mixed-bit pools; not the headline)
     python bench.py --comix      (the CoMixKV controller instead: its own JSON line)
+    python bench.py --rotation-ablation   (plain FWHT vs randomized rotation: its own JSON line)
 """
 from __future__ import annotations
 
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--comix", action="store_true",
                     help="instead of the decode job: time the CoMixKV controller (sensitivity kernel + allocation) "
                          "on the Qwen3-32B shape and measure the attention error of its bits against uniform 3 bits")
+    ap.add_argument("--rotation-ablation", action="store_true",
+                    help="instead of the decode job: attention error and pool-kernel time of the plain FWHT "
+                         "against a randomized (signed) rotation, on Gaussian and on Hadamard-aligned V")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -131,6 +135,9 @@ def main():
         return
     if args.comix:
         comix_bench()
+        return
+    if args.rotation_ablation:
+        rotation_ablation()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
@@ -421,6 +428,85 @@ def qwen_bench(args):
         "pool_build_us": float(np.mean(build_ms)) * 1e3,
         "decode_step_us": (ms_per_step - float(np.mean(build_ms))) / NS * 1e3,
     }), flush=True)
+
+
+def rotation_ablation():
+    """Plain FWHT against a randomized rotation (signs before the FWHT), Llama-3-8B shape.
+
+    One agent (4 query rows per kv head) over a 4096-token pool of 32 layers, 8 kv heads,
+    d 128, 3 bits.  V recipes (bf16, device-seeded): "gaussian" = N(0, 1) * LogNormal(0, 0.5)
+    channel scales (the workloads' recipe); "hadamard_aligned" = each token's V a Hadamard
+    row of the head dimension times a LogNormal(0, 1) magnitude plus 1% Gaussian noise
+    (structured V that the plain transform concentrates into one coordinate).  Error: decode
+    of 8 query steps over the pool against exact attention over the same bf16 K/V (the same
+    call with an empty pool and the tokens as native suffix); relative L2 per output row.
+    """
+    import torch
+
+    import workloads as wl
+    from quantized_shared_kv_amd import polykv as pk
+
+    pk.lib()
+    dev = "cuda:0"
+    L, Hkv, Hq, d, T, R = 32, 8, 32, 128, 4096, 8
+    signs = wl.rotation_signs(0, d)
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    q = torch.randn((R, 1, L, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    sk = torch.exp(0.5 * torch.randn((L, Hkv, 1, d), generator=g, device=dev))
+    k = (torch.randn((L, Hkv, T, d), generator=g, device=dev) * sk).to(torch.bfloat16)
+    h = torch.ones((1, 1), device=dev)
+    while h.shape[0] < d:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    recipes = {
+        "gaussian": (torch.randn((L, Hkv, T, d), generator=g, device=dev)
+                     * torch.exp(0.5 * torch.randn((L, Hkv, 1, d), generator=g, device=dev))).to(torch.bfloat16),
+        "hadamard_aligned": (h[torch.randint(0, d, (L, Hkv, T), generator=g, device=dev)]
+                             * torch.exp(torch.randn((L, Hkv, T, 1), generator=g, device=dev))
+                             + 0.01 * torch.randn((L, Hkv, T, d), generator=g, device=dev)).to(torch.bfloat16),
+    }
+    empty_cfg = pk.make_config(L, Hkv, d, 32, [3] * L)
+    ebuf = torch.empty(pk.pool_bytes(empty_cfg), dtype=torch.uint8, device=dev)
+    empty = pk.pool_build(empty_cfg, ebuf.data_ptr(), ebuf.numel())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()  # creates the underlying events
+    e1.record()
+    res = {}
+    for name, v in recipes.items():
+        ref = torch.empty((1, L, Hq, d), dtype=torch.float32, device=dev)
+        out = torch.empty_like(ref)
+        kw, vw = k.unsqueeze(0).contiguous(), v.unsqueeze(0).contiguous()
+        res[name] = {}
+        for variant, sg in (("plain_fwht", None), ("signed_rotation", signs)):
+            cfg = pk.make_config(L, Hkv, d, T, [3] * L, v_signs=sg)
+            buf = torch.empty(pk.pool_bytes(cfg), dtype=torch.uint8, device=dev)
+            pool = pk.pool_build(cfg, buf.data_ptr(), buf.numel())
+            pk.pool_quantize_append(pool, 0, k, v)
+            ws = torch.empty(max(pk.agent_decode_attention([pool], q[0], out, 0),
+                                 pk.agent_decode_attention([empty], q[0], ref, 0, kw, vw, [T])), dtype=torch.uint8,
+                             device=dev)
+            errs = []
+            for r in range(R):
+                pk.agent_decode_attention([pool], q[r], out, 0, workspace=ws)
+                pk.agent_decode_attention([empty], q[r], ref, 0, kw, vw, [T], workspace=ws)
+                errs.append(((out - ref).double().norm(dim=-1) / ref.double().norm(dim=-1)).flatten())
+            e = torch.cat(errs)
+            ts = []
+            for r in range(12):
+                pk.agent_decode_attention([pool], q[r % R], out, 0, workspace=ws, pool_events=(e0, e1))
+                torch.cuda.synchronize()
+                ts.append(1e3 * e0.elapsed_time(e1))
+            res[name][variant] = {"attention_rel_error_mean": float(e.mean()),
+                                  "attention_rel_error_max": float(e.max()),
+                                  "pool_kernel_us": float(np.median(ts[2:]))}
+            del buf
+        log(f"[rotation] {name}: {json.dumps(res[name])}")
+    print(json.dumps({"metric": "V codec ablation: plain FWHT vs randomized rotation (attention error, kernel time)",
+                      "value": res["hadamard_aligned"]["signed_rotation"]["attention_rel_error_mean"],
+                      "unit": "relative L2 error", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": "llama3_8b_shape_1_agent", "layers": L, "kv_heads": Hkv, "q_heads": Hq,
+                                 "head_dim": d, "pool_tokens": T, "v_bits": 3, "query_steps": R},
+                      "results": res}), flush=True)
 
 
 def comix_bench():
