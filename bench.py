@@ -45,8 +45,11 @@ def parse():
                     help="extra untimed pool-kernel launches, each after a 512 MiB cache flush")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                             "pool_decode_traffic.json"))
-    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "qwen3_32b_comix"],
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "llama3_8b_long", "smollm2", "qwen3_32b_comix"],
                     help="llama3_8b (default, the headline): one shared 4096-token pool, 15 agents; "
+                         "llama3_8b_long: 7194-token pool, 256-token native windows, 32 decode calls; "
+                         "smollm2: 24 layers, 32 MHA heads, d 64, 1851 tokens, 3 agents; "
                          "qwen3_32b_comix: 8 agents with their own 8064-token mixed 2/3/4-bit pools")
     ap.add_argument("--comix", action="store_true",
                     help="instead of the decode job: time the CoMixKV controller (sensitivity kernel + allocation) "
@@ -153,8 +156,11 @@ def main():
 
     pk.lib()  # fails loudly if the HIP library is not built
     kernel = {"default": pk.KERNEL_DEFAULT, "valu": pk.KERNEL_VALU, "mfma": pk.KERNEL_MFMA}[args.kernel]
-    w = wl.LLAMA3_8B
+    w = {"llama3_8b": wl.LLAMA3_8B, "llama3_8b_long": wl.LLAMA3_8B_LONG, "smollm2": wl.SMOLLM2}[args.workload]
     steps_per_job = args.decode_steps or w.steps
+
+    def sfx_lens(s):  # native tokens per agent at decode step s: growing window, or a fixed one
+        return [w.sfx_len(s)] * A
     dev = "cuda:0"
     L, Hkv, Hq, d, T, A, S = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens, w.n_agents, w.sfx_tokens
 
@@ -235,7 +241,7 @@ def main():
         if timed_kernels:
             b1.record()
         for s in range(steps_per_job):
-            lens = [min(s + 1, S)] * A
+            lens = sfx_lens(s)
             pk.agent_decode_attention(pools, q_all[s], out, 0, sfx_k, sfx_v, lens, workspace=ws, kernel=kernel,
                                       pool_events=evs[s] if timed_kernels and s % EV_EVERY == 0 else None,
                                       private_pools=prv_pools)
@@ -308,7 +314,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "agents": A, "decode_steps_per_step": steps_per_job, "pool_tokens": T,
                    "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "v_bits": 3,
-                   "suffix": f"bf16, s+1 tokens at decode step s (max {S})", "kernel": args.kernel,
+                   "suffix": (f"bf16, s+1 tokens at decode step s (max {S})" if w.sfx_mode == "grow"
+                              else f"bf16, {S} tokens per agent"), "kernel": args.kernel,
                    **({"private_tokens_per_agent": NP} if NP else {})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
@@ -648,7 +655,7 @@ def cpu_baseline(w, steps_per_job):
         q = np.stack([w.queries(s, a).f32[:nl] for a in range(A)])
         t1 = time.perf_counter()
         attention.decode_call(q, [0] * A, decoded, lambda a, l: sk[a][l], lambda a, l: sv[a][l],
-                              [min(s + 1, w.sfx_tokens)] * A, w.n_kv_heads)
+                              [w.sfx_len(s)] * A, w.n_kv_heads)
         t_dec += time.perf_counter() - t1
     t_step = t_dec / ns
     job = (L / nl) * (t_build + steps_per_job * t_step)
