@@ -25,8 +25,19 @@ def to_device(t) -> torch.Tensor:
 class DevicePool:
     """A pool in a torch-owned device buffer."""
 
-    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits):
-        self.cfg = pk.make_config(n_layers, n_kv_heads, head_dim, capacity, bits)
+    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=None):
+        self._allocate(pk.make_config(n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=v_signs))
+
+    @classmethod
+    def empty_for(cls, cfg) -> "DevicePool":
+        """A buffer of pool_bytes(cfg) bytes with no descriptor built yet (self.pool unset)."""
+        dp = cls.__new__(cls)
+        dp.cfg = cfg
+        dp.buf = torch.empty(pk.pool_bytes(cfg), dtype=torch.uint8, device=DEV)
+        return dp
+
+    def _allocate(self, cfg):
+        self.cfg = cfg
         n = pk.pool_bytes(self.cfg)
         assert n > 0
         self.buf = torch.empty(n, dtype=torch.uint8, device=DEV)

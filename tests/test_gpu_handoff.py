@@ -72,10 +72,7 @@ def test_shards_reproduce_the_whole_pool(kernel):
     want = oracle_decode(q32, [0] * A, [ref], fk, fv, lens, H)
     assert attention.max_rel_error(whole, want) <= 1e-3
     for h0, hc in ((0, 1), (1, 2), (3, 1)):
-        cfg = pk.make_config(L, hc, d, w.pool_tokens, w.v_bits(0))
-        sbuf = DevicePool.__new__(DevicePool)
-        sbuf.cfg = cfg
-        sbuf.buf = torch.empty(pk.pool_bytes(cfg), dtype=torch.uint8, device=DEV)
+        sbuf = DevicePool.empty_for(pk.make_config(L, hc, d, w.pool_tokens, w.v_bits(0)))
         sbuf.pool = pk.pool_shard(dp.pool, h0, hc, sbuf.buf.data_ptr(), sbuf.buf.numel())
         assert list(sbuf.pool.n_tokens[:L]) == list(dp.pool.n_tokens[:L])
         bad = compare_image(sbuf, ref.shard(h0, hc))

@@ -36,11 +36,7 @@ def signed_pair(w, pool_id, signs, layers=None, chunks=None, capacity=None):
     L = w.n_layers if layers is None else layers
     cap = capacity or w.pool_tokens
     bits = w.v_bits(pool_id)[:L]
-    dp = DevicePool.__new__(DevicePool)
-    dp.cfg = pk.make_config(L, w.n_kv_heads, w.head_dim, cap, bits, v_signs=signs)
-    n = pk.pool_bytes(dp.cfg)
-    dp.buf = torch.empty(n, dtype=torch.uint8, device=DEV)
-    dp.pool = pk.pool_build(dp.cfg, dp.buf.data_ptr(), n)
+    dp = DevicePool(L, w.n_kv_heads, w.head_dim, cap, bits, v_signs=signs)
     ref = pool_image.PoolImage(L, w.n_kv_heads, w.head_dim, cap, bits, signs)
     ks = [w.pool_k(pool_id, l) for l in range(L)]
     vs = [w.pool_v(pool_id, l) for l in range(L)]
