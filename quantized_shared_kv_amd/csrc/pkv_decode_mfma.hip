@@ -60,12 +60,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kStep = 32;         // tokens per wavefront step
-constexpr int kStages = 4;        // LDS ring depth per wavefront (kStages - 1 steps in flight)
 constexpr float kLazy = 8.0f;     // scores may exceed the reference by up to 2^8 (fp16 weights)
 constexpr float kMargin = 8.0f;   // reference = first step's row max + this (log2 units)
 constexpr int kLutCopies = 32;
 constexpr int kWeightExp = 7;     // weights are scaled into [0, 2^15)
-constexpr int kStageBytes = 32 * 128 + 64 * 32 + 256;  // K + V codes + norms/scales, largest case
+// LDS ring per wavefront: kStages slots (kStages - 1 steps in flight) of kStageBytes (K, V codes
+// at 4 bits, norms and scales of one 32-token step).  At head_dim 64 a stage is half the size
+// and three slots keep a workgroup under half the LDS, so two workgroups share a compute unit
+// and one's set-up and finish overlap the other's stream (short pools run many workgroups).
+template <int D>
+struct Ring {
+    static constexpr int kStages = D == 64 ? 3 : 4;
+    static constexpr int kStageBytes = 32 * D + 16 * D + 256;
+};
 
 struct CentArg {
     float c[3][16];
@@ -82,15 +89,23 @@ union H8 {
 // the LUT of centroid pairs.  After it: every wavefront's rotated-domain
 // accumulator tile [64 rows][D], combined in a fixed order.
 constexpr int kMaxRows = 64;
+template <int D>
 struct LoopLds {
     uint32_t lut[256 * kLutCopies];  // first, so its address has zero low 15 bits
-    uint8_t ring[kWaves][kStages][kStageBytes];
+    uint8_t ring[kWaves][Ring<D>::kStages][Ring<D>::kStageBytes];
 };
+template <int D>
 union BigLds {
-    LoopLds loop;
-    float accs[kWaves * kMaxRows * 128];
+    LoopLds<D> loop;
+    float accs[kWaves * kMaxRows * D];
 };
-__shared__ __align__(32768) BigLds g_big;
+__shared__ __align__(32768) BigLds<128> g_big128;
+__shared__ __align__(32768) BigLds<64> g_big64;
+template <int D>
+__device__ __forceinline__ BigLds<D>& big_lds() {
+    if constexpr (D == 128) return g_big128;
+    else return g_big64;
+}
 __shared__ float g_m[kWaves][64];
 __shared__ float g_l[kWaves][64];
 __shared__ int g_flag;
@@ -347,7 +362,7 @@ struct StageLayout {
     static constexpr int VOFF = NK * 1024;
     static constexpr int NOFF = VOFF + NV * VSTRIDE;  // norms [32] then scales [32]
     static constexpr int NDMA = NK + NV + 1;          // direct-to-LDS instructions per stage
-    static_assert(NOFF + 256 <= kStageBytes, "stage overflow");
+    static_assert(NOFF + 256 <= Ring<D>::kStageBytes, "stage overflow");
 };
 
 // Always inlined: an out-of-line body would receive the launch struct by reference,
@@ -393,6 +408,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     const int my_steps = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
     // K row of this lane in tile u: token 8*(rl>>2) + 4u + (rl&3), bytes lg*DL .. lg*DL + DL
     const int ktok0 = 8 * (rl >> 2) + (rl & 3);
+    using RG = Ring<D>;
+    BigLds<D>& g_big = big_lds<D>();
     uint8_t* ring = &g_big.loop.ring[wave][0][0];
 
     // Per-lane byte offsets of a step's pieces, fixed across steps: each load below is a
@@ -407,9 +424,9 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // norms (lanes 0-31) and K scales (lanes 32-63) of the step's 32 tokens
     const bool nlane = lane < 32;
     const uint32_t noff = 4u * (uint32_t)(lane & 31);
-    auto issue = [&](int it) {  // DMA of this wavefront's it-th step into ring slot it % kStages
+    auto issue = [&](int it) {  // DMA of this wavefront's it-th step into ring slot it % RG::kStages
         const int t0 = tb + (wave + it * kWaves) * kStep;
-        uint8_t* st = ring + (it % kStages) * kStageBytes;
+        uint8_t* st = ring + (it % RG::kStages) * RG::kStageBytes;
         const int8_t* kstep = kq + (uint64_t)t0 * D;
 #pragma unroll
         for (int i = 0; i < SL::NK; ++i) dma<16>(kstep, koff[i], st + SL::KOFF + i * 1024);
@@ -476,7 +493,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x
 
 #pragma unroll
-    for (int it = 0; it < kStages - 1; ++it)
+    for (int it = 0; it < RG::kStages - 1; ++it)
         if (it < my_steps) issue(it);
 
     // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i);
@@ -576,7 +593,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // ring slot of step `it` -> registers (no wait: see ring_fence)
     using Raw = RingRaw<SL::NK, CB>;
     auto ring_issue = [&](int it, Raw& r) {
-        const uint32_t sa = ring_a + (it % kStages) * kStageBytes;
+        const uint32_t sa = ring_a + (it % RG::kStages) * RG::kStageBytes;
         ring_read<SL::NK, CB>(sa + SL::KOFF + lane * 16, sa + SL::VOFF + lane * SL::VLANE, sa + SL::NOFF + 32 * lg, r);
     };
     // K as fp16 operands (1152 + k, exact; the offset is removed by the accumulator init)
@@ -628,7 +645,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) cref[rt] = 0.0f;
     if (my_steps > 0) {
-        wait_groups(min(my_steps, kStages - 1) - 1);  // steps 0 .. kStages - 2 were issued
+        wait_groups(min(my_steps, RG::kStages - 1) - 1);  // steps 0 .. RG::kStages - 2 were issued
         Raw r;
         ring_issue(0, r);
         ring_fence(r);
@@ -662,7 +679,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
         if (pass == 1) {
 #pragma unroll
-            for (int it = 0; it < kStages - 1; ++it)
+            for (int it = 0; it < RG::kStages - 1; ++it)
                 if (it < my_steps) issue(it);
         }
         // One 32-token step.  The ring reads of the next step are issued once this
@@ -678,8 +695,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             constexpr bool TAIL = decltype(tail_tag)::value;
             const int t0 = tb + (wave + it * kWaves) * kStep;
             if (prefetch) {
-                if (it + kStages - 1 < my_steps) issue(it + kStages - 1);  // slot of step it - 1, already read
-                wait_groups(min(kStages - 2, my_steps - 2 - it));       // loads of step it + 1 landed
+                if (it + RG::kStages - 1 < my_steps) issue(it + RG::kStages - 1);  // slot of step it - 1, already read
+                wait_groups(min(RG::kStages - 2, my_steps - 2 - it));       // loads of step it + 1 landed
             }
             Chunk<CB> ch;
             raw.code_words(ch.w);
@@ -734,7 +751,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         const int full = my_steps - (has_tail ? 1 : 0);
         Raw raw;
         if (my_steps > 0) {
-            wait_groups(min(my_steps - 1, kStages - 2));
+            wait_groups(min(my_steps - 1, RG::kStages - 2));
             ring_issue(0, raw);
             ring_fence(raw);
         }
