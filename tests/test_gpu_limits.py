@@ -70,3 +70,27 @@ def test_128_layers_and_a_layer_subrange():
         want = attention.decode_call(q32, [0, 0], lambda p, l, g: ref.decoded_layer(lb + l, g), None, None, [0, 0],
                                      w.n_kv_heads)
         assert attention.max_rel_error(out, want) <= TOL, (lb, lc)
+
+
+@pytest.mark.parametrize("kernel", [pk.KERNEL_MFMA, pk.KERNEL_VALU])
+@pytest.mark.parametrize("scale", [0.05, 0.37])
+def test_explicit_softmax_scale(kernel, scale):
+    """A caller-given softmax scale instead of 1/sqrt(d) (0.37 is ~4x the default at d 128:
+    a sharper softmax, so scores leave the first step's reference faster)."""
+    print(f"[limits] softmax scale {scale} kernel {kernel}", flush=True)
+    from oracle import attention as att
+
+    from gpu_helpers import DEV
+
+    w = wl.LLAMA3_8B.replace(n_layers=2, n_kv_heads=2, n_q_heads=8, pool_tokens=150, n_agents=3, sfx_tokens=11)
+    dp, ref = build_pair(w, 0)
+    q, q32 = make_queries(w, 0, range(3))
+    sk, sv, fk, fv = make_suffix(w, range(3), 2)
+    lens = [0, 4, 11]
+    out = torch.empty((3, 2, 8, 128), dtype=torch.float32, device=DEV)
+    wsb = pk.agent_decode_attention([dp.pool] * 3, q, out, 0, sk, sv, lens, softmax_scale=scale, kernel=kernel)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+    pk.agent_decode_attention([dp.pool] * 3, q, out, 0, sk, sv, lens, workspace=ws, softmax_scale=scale, kernel=kernel)
+    torch.cuda.synchronize()
+    want = att.decode_call(q32, [0] * 3, lambda p, l, g: ref.decoded_layer(l, g), fk, fv, lens, 2, sigma=scale)
+    assert att.max_rel_error(out.cpu().numpy().astype(np.float64), want) <= TOL
