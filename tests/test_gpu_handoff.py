@@ -81,3 +81,45 @@ def test_shards_reproduce_the_whole_pool(kernel):
         sks, svs = sk[:, :, h0:h0 + hc].contiguous(), sv[:, :, h0:h0 + hc].contiguous()
         part = run_decode([sbuf.pool] * A, qs, (sks, svs), lens, kernel=kernel, splits=1)
         assert np.array_equal(part, whole[:, :, h0 * G:(h0 + hc) * G]), (h0, hc)
+
+
+def test_shards_at_the_llama3_8b_shape():
+    """Full Llama-3-8B pool (32 layers, 8 kv heads, 4096 tokens, 15 agents, 128-token windows) split
+    into 8 one-head shards: every region of each shard equals the matching slice of the whole image,
+    and each shard's decode equals the whole pool's rows for its heads bit for bit (one split each)."""
+    print("[handoff] llama3-8b shards", flush=True)
+    L, H, Hq, d, T, A, S = 32, 8, 32, 128, 4096, 15, 128
+    G = Hq // H
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    k = (torch.randn((L, H, T, d), generator=g, device=DEV) * 1.3).to(torch.bfloat16)
+    v = torch.randn((L, H, T, d), generator=g, device=DEV).to(torch.bfloat16)
+    whole = DevicePool(L, H, d, T, [3] * L)
+    whole.append(0, k, v)
+    q = torch.randn((A, L, Hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    sk = torch.randn((A, L, H, S, d), generator=g, device=DEV).to(torch.bfloat16)
+    sv = torch.randn((A, L, H, S, d), generator=g, device=DEV).to(torch.bfloat16)
+    lens = [1 + 9 * a for a in range(A)]
+    ref = run_decode([whole.pool] * A, q, (sk, sv), lens, splits=1)
+    img = whole.buf
+    P = whole.pool
+    tc = P.tc
+    for h in range(H):
+        sh = DevicePool.empty_for(pk.make_config(L, 1, d, T, [3] * L))
+        sh.pool = pk.pool_shard(P, h, 1, sh.buf.data_ptr(), sh.buf.numel())
+        Q = sh.pool
+        b = sh.buf
+        torch.cuda.synchronize()
+        kq_w = img[P.off_kq:P.off_kq + L * H * tc * d].view(L, H, tc * d)[:, h]
+        assert torch.equal(b[Q.off_kq:Q.off_kq + L * tc * d].view(L, tc * d), kq_w)
+        vn_w = img[P.off_vn:P.off_vn + L * H * tc * 4].view(L, H, tc * 4)[:, h]
+        assert torch.equal(b[Q.off_vn:Q.off_vn + L * tc * 4].view(L, tc * 4), vn_w)
+        assert torch.equal(b[Q.off_ks:Q.off_ks + L * tc * 4], img[P.off_ks:P.off_ks + L * tc * 4])
+        vm_w = img[P.off_vmax:P.off_vmax + L * H * 4].view(L, H, 4)[:, h]
+        assert torch.equal(b[Q.off_vmax:Q.off_vmax + L * 4].view(L, 4), vm_w)
+        for l in range(L):
+            n = (tc // 8) * d * 3
+            assert torch.equal(b[Q.off_vc[l]:Q.off_vc[l] + n], img[P.off_vc[l] + h * n:P.off_vc[l] + (h + 1) * n])
+        part = run_decode([Q] * A, q[:, :, h * G:(h + 1) * G].contiguous(),
+                          (sk[:, :, h:h + 1].contiguous(), sv[:, :, h:h + 1].contiguous()), lens, splits=1)
+        assert np.array_equal(part, ref[:, :, h * G:(h + 1) * G]), h
