@@ -4,7 +4,7 @@ PolyKV explainer, section 2.A (SharedKVPool): the shared context is encoded
 once into one object; its memory does not depend on how many agents read it.
 Section 4 (memory efficiency) reports the pool as constant in the agent count.
 
-The layout is this build's choice (the pages give none).  For a pool of
+The layout is a choice made here (the pages give none).  For a pool of
 L layers, Hkv kv heads, head dim d, capacity rounded up to tc (a multiple of
 32 tokens) and per-layer V bit widths b_l, regions follow each other in this
 order, each starting on a 256-byte boundary:
