@@ -661,7 +661,7 @@ def cpu_baseline(w, steps_per_job):
     job = (L / nl) * (t_build + steps_per_job * t_step)
     return {"value": A * steps_per_job / job, "unit": "agent-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"layers 0-{nl - 1}: pool build ({t_build:.2f}s) + decode steps 0-{ns - 1} for {A} agents "
-                      f"({t_step:.2f}s per step), scaled x{L // nl} layers and x{steps_per_job} decode steps",
+                      f"({t_step:.2f}s per step), scaled x{L / nl:g} layers and x{steps_per_job} decode steps",
             "sample_seconds": t_build + t_dec}
 
 
