@@ -3,8 +3,10 @@
     python -m quantized_shared_kv_amd.build
 
 The library is written to quantized_shared_kv_amd/_lib/libpolykv.so.  Every
-HIP translation unit is compiled with packed-fp32 instructions disabled, and
-matrix-core instructions write VGPRs (-amdgpu-mfma-vgpr-form).
+translation unit is compiled to its own object in parallel (``_lib/obj/``),
+then linked.  Every HIP translation unit is compiled with packed-fp32
+instructions disabled, and matrix-core instructions write VGPRs
+(-amdgpu-mfma-vgpr-form).
 """
 from __future__ import annotations
 
@@ -12,13 +14,16 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
+OBJ_DIR = os.path.join(OUT_DIR, "obj")
 LIB = os.path.join(OUT_DIR, "libpolykv.so")
-SOURCES = ["pkv_host.cpp", "pkv_quantize.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_comix.hip", "pkv_handoff.cpp"]
+SOURCES = ["pkv_host.cpp", "pkv_quantize.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_comix.hip",
+           "pkv_handoff.cpp"]
 ARCH = "gfx950"
 
 
@@ -29,26 +34,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # matrix-core results in VGPRs: the score tiles are read by vector instructions, so
-           # accumulating them in AGPRs cost a copy per value (the query operands sit in AGPRs)
-           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wno-unused-command-line-argument",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core results in VGPRs: the score tiles are read by vector instructions, so
+            # accumulating them in AGPRs cost a copy per value (the query operands sit in AGPRs)
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            "-Wno-unused-command-line-argument",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                     if "packed-fp32-ops" not in l and l.strip())
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
-    if verbose and errs:
-        print(errs, flush=True)
+    errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip())
+    return r.returncode, errs
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o")
+        jobs.append((obj, [cc] + _flags() + ["-c", "-o", obj, os.path.join(CSRC, s)]))
+    if verbose:
+        for _, cmd in jobs:
+            print(" ".join(cmd), flush=True)
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(lambda j: _run(j[1]), jobs))
+    for (obj, _), (rc, errs) in zip(jobs, results):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed for {os.path.basename(obj)} ({rc}):\n{errs}")
+        if verbose and errs:
+            print(errs, flush=True)
+    tmp = LIB + ".tmp"
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in jobs]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, errs = _run(link)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{errs}")
     os.replace(tmp, LIB)
     return LIB
 

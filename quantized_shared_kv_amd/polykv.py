@@ -163,7 +163,7 @@ def pool_quantize_append(pool: Pool, layer_begin: int, k, v, stream=None) -> Non
     """k, v: device tensors [layer_count][n_kv_heads][n_tokens][head_dim], fp32 or bf16."""
     if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
         raise ValueError("k and v must be equal-shape 4-D tensors")
-    if not (k.is_contiguous() and v.is_contiguous()) or not k.is_cuda:
+    if not (k.is_contiguous() and v.is_contiguous()) or not (k.is_cuda and v.is_cuda):
         raise ValueError("k and v must be contiguous device tensors")
     nl, hkv, n, d = k.shape
     if hkv != pool.cfg.n_kv_heads or d != pool.cfg.head_dim:
@@ -175,12 +175,21 @@ def pool_quantize_append(pool: Pool, layer_begin: int, k, v, stream=None) -> Non
 
 def _decode_args(pools, q, out, layer_begin, sfx_k=None, sfx_v=None, sfx_len=None, softmax_scale=0.0,
                  kernel=KERNEL_DEFAULT, splits=0, pool_events=None, private_pools=None):
+    import torch
+
     n_agents = len(pools)
     arr = (POINTER(Pool) * max(n_agents, 1))(*[ctypes.pointer(p) for p in pools])
     lens = (c_int32 * max(n_agents, 1))(*(list(sfx_len) if sfx_len is not None else [0] * n_agents))
+    if q.dim() != 4:
+        raise ValueError("q must be [n_agents][layers][n_q_heads][head_dim]")
     A, lc, hq, d = q.shape
     if A != n_agents or tuple(out.shape) != (A, lc, hq, d) or not q.is_contiguous() or not out.is_contiguous():
         raise ValueError("q/out must be contiguous [n_agents][layers][n_q_heads][head_dim]")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32 (the kernels write fp32 outputs)")
+    _dtype_code(q)
+    if not (q.is_cuda and out.is_cuda):
+        raise ValueError("q and out must be device tensors")
     a = DecodeArgs()
     a.n_agents, a.n_q_heads, a.layer_begin, a.layer_count = n_agents, hq, layer_begin, lc
     a.softmax_scale = softmax_scale
@@ -188,9 +197,20 @@ def _decode_args(pools, q, out, layer_begin, sfx_k=None, sfx_v=None, sfx_len=Non
     a.q = q.data_ptr()
     a.q_dtype = _dtype_code(q)
     a.out = out.data_ptr()
+    if (sfx_k is None) != (sfx_v is None):
+        raise ValueError("sfx_k and sfx_v are given together")
     if sfx_k is not None:
         if sfx_k.shape != sfx_v.shape or sfx_k.dim() != 5 or not sfx_k.is_contiguous() or not sfx_v.is_contiguous():
             raise ValueError("sfx_k/sfx_v must be contiguous [n_agents][layers][n_kv_heads][sfx_cap][head_dim]")
+        hkv = pools[0].cfg.n_kv_heads if n_agents else sfx_k.shape[2]
+        if tuple(sfx_k.shape[:3]) != (A, lc, hkv) or sfx_k.shape[4] != d:
+            raise ValueError(f"sfx_k/sfx_v shape {tuple(sfx_k.shape)} does not match "
+                             f"[n_agents={A}][layers={lc}][n_kv_heads={hkv}][sfx_cap][head_dim={d}]")
+        if sfx_k.dtype != sfx_v.dtype:
+            raise ValueError("sfx_k and sfx_v must have the same dtype")
+        _dtype_code(sfx_k)
+        if not (sfx_k.is_cuda and sfx_v.is_cuda):
+            raise ValueError("sfx_k and sfx_v must be device tensors")
         a.sfx_k, a.sfx_v = sfx_k.data_ptr(), sfx_v.data_ptr()
         a.sfx_dtype = _dtype_code(sfx_k)
         a.sfx_cap = sfx_k.shape[3]
@@ -265,6 +285,8 @@ def comix_sensitivity(q, win_k, win_v, win_len, out, softmax_scale=0.0, stream=N
     if not (win_k.is_contiguous() and win_v.is_contiguous()) or win_k.shape != win_v.shape or \
             win_k.dim() != 5 or tuple(win_k.shape[:2]) != (A, L) or win_k.shape[4] != d or win_k.dtype != win_v.dtype:
         raise ValueError("windows must be contiguous [A][L][Hkv][cap][d], same shape and dtype")
+    if not (q.is_cuda and out.is_cuda and win_k.is_cuda and win_v.is_cuda):
+        raise ValueError("q, windows and out must be device tensors")
     lens = (c_int32 * A)(*[int(x) for x in win_len])
     a = ComixArgs(A, L, Hq, int(win_k.shape[2]), d, float(softmax_scale), R, c_void_p(q.data_ptr()), _dtype_code(q),
                   c_void_p(win_k.data_ptr()), c_void_p(win_v.data_ptr()), _dtype_code(win_k), int(win_k.shape[3]),

@@ -129,12 +129,13 @@ def test_quantize_append_validation_errors():
 class _FakeT:
     """Minimal stand-in with the attributes the binding reads, for host-only calls."""
 
-    def __init__(self, shape, ptr, dtype="bf16"):
+    def __init__(self, shape, ptr, dtype="bf16", is_cuda=True):
         import torch
 
         self.shape = tuple(shape)
         self._ptr = ptr
-        self.dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[dtype]
+        self.is_cuda = is_cuda
 
     def data_ptr(self):
         return self._ptr
@@ -162,7 +163,7 @@ def test_decode_workspace_query_and_errors():
     with pytest.raises(pk.PolyKVError):  # sfx_len beyond capacity
         pk.agent_decode_attention([pool] * A, q, out, sfx_k=sk, sfx_v=sk, sfx_len=[0, 5, 17])
     with pytest.raises(pk.PolyKVError):  # heads not a multiple of kv heads
-        pk.agent_decode_attention([pool] * A, _FakeT((A, lc, 3, d), 1 << 24), _FakeT((A, lc, 3, d), 1 << 25))
+        pk.agent_decode_attention([pool] * A, _FakeT((A, lc, 3, d), 1 << 24), _FakeT((A, lc, 3, d), 1 << 25, "f32"))
     with pytest.raises(pk.PolyKVError):  # layers beyond the pool
         pk.agent_decode_attention([pool] * A, q, out, layer_begin=1)
     other = _fake_pool(L=2, H=2, d=128, cap=100)
@@ -250,3 +251,62 @@ def test_rotation_signs_in_the_config():
     assert pk.pool_bytes(cfg) == 0
     with pytest.raises(ValueError):
         pk.make_config(2, 2, 64, 40, [3, 3], v_signs=s[:10])
+
+
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """The binding checks what the C side cannot see (dtypes, devices, suffix shapes) and
+    raises ValueError before the library is called, so no kernel can write past a buffer."""
+    pool = _fake_pool(L=2, H=2, d=64, cap=100)
+    pool.n_tokens[0] = pool.n_tokens[1] = 70
+    A, lc, hq, d = 3, 2, 4, 64
+    q = _FakeT((A, lc, hq, d), 1 << 24)
+    out = _FakeT((A, lc, hq, d), 1 << 25, "f32")
+    sk = _FakeT((A, lc, 2, 16, d), 1 << 26)
+    sv = _FakeT((A, lc, 2, 16, d), 1 << 27)
+    pk.agent_decode_attention([pool] * A, q, out, sfx_k=sk, sfx_v=sv, sfx_len=[0, 5, 16])  # the good call
+    bad_calls = {
+        "bf16 out": dict(out=_FakeT((A, lc, hq, d), 1 << 25, "bf16")),
+        "fp16 out": dict(out=_FakeT((A, lc, hq, d), 1 << 25, "f16")),
+        "fp16 q": dict(q=_FakeT((A, lc, hq, d), 1 << 24, "f16")),
+        "host q": dict(q=_FakeT((A, lc, hq, d), 1 << 24, is_cuda=False)),
+        "host out": dict(out=_FakeT((A, lc, hq, d), 1 << 25, "f32", is_cuda=False)),
+        "fp32 sfx_v with bf16 sfx_k": dict(sfx_v=_FakeT((A, lc, 2, 16, d), 1 << 27, "f32")),
+        "suffix with fewer layers": dict(sfx_k=_FakeT((A, 1, 2, 16, d), 1 << 26), sfx_v=_FakeT((A, 1, 2, 16, d), 1 << 27)),
+        "suffix with fewer agents": dict(sfx_k=_FakeT((2, lc, 2, 16, d), 1 << 26),
+                                         sfx_v=_FakeT((2, lc, 2, 16, d), 1 << 27)),
+        "suffix with other kv heads": dict(sfx_k=_FakeT((A, lc, 1, 16, d), 1 << 26),
+                                           sfx_v=_FakeT((A, lc, 1, 16, d), 1 << 27)),
+        "suffix with other head_dim": dict(sfx_k=_FakeT((A, lc, 2, 16, 2 * d), 1 << 26),
+                                           sfx_v=_FakeT((A, lc, 2, 16, 2 * d), 1 << 27)),
+        "host suffix": dict(sfx_k=_FakeT((A, lc, 2, 16, d), 1 << 26, is_cuda=False),
+                            sfx_v=_FakeT((A, lc, 2, 16, d), 1 << 27, is_cuda=False)),
+        "fp16 suffix": dict(sfx_k=_FakeT((A, lc, 2, 16, d), 1 << 26, "f16"),
+                            sfx_v=_FakeT((A, lc, 2, 16, d), 1 << 27, "f16")),
+        "sfx_k without sfx_v": dict(sfx_v=None),
+    }
+    for what, kw in bad_calls.items():
+        args = dict(q=q, out=out, sfx_k=sk, sfx_v=sv)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError), match=""):
+            pk.agent_decode_attention([pool] * A, args["q"], args["out"], sfx_k=args["sfx_k"], sfx_v=args["sfx_v"],
+                                      sfx_len=[0, 5, 16])
+        # and the same with a workspace: still rejected before the library is reached
+        with pytest.raises((ValueError, TypeError)):
+            pk.agent_decode_attention([pool] * A, args["q"], args["out"], sfx_k=args["sfx_k"], sfx_v=args["sfx_v"],
+                                      sfx_len=[0, 5, 16], workspace=_FakeWs(1 << 28, 1 << 20)), what
+
+
+class _FakeWs:
+    """A workspace stand-in that must never reach the library in the tests that use it."""
+
+    def __init__(self, ptr, n):
+        self._ptr, self._n = ptr, n
+
+    def data_ptr(self):
+        raise AssertionError("the binding reached the library call")
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
