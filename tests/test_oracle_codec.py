@@ -207,3 +207,65 @@ def test_signs_from_mask_bit_order():
     m = bytes([0b00000101] + [0] * 15)
     s = codec.signs_from_mask(m, 128)
     assert s[0] == -1 and s[1] == 1 and s[2] == -1 and np.all(s[3:] == 1)
+
+
+# ---- last-bit conventions, pinned by hand-worked fp32 examples ---------------------------------
+# Each example is an input on which the plausible alternative readings give different bytes.
+# The intermediate values are written out as fp32 bit patterns so that each step can be checked
+# with any correctly rounded fp32 calculator; the assertions are on the oracle's own output.
+
+def _f(bits: int) -> np.float32:
+    return np.frombuffer(int(bits).to_bytes(4, "little"), dtype=np.float32)[0]
+
+
+def test_fwht_stage_order_is_ascending_half_width():
+    """PolyKV explainer, section 2.B names the FWHT; the reading fixes butterflies with half-width
+    1, 2, 4, ... (ascending).  x = (1, e, -1, 0, 0, ...), e = 2^-24, d = 128:
+      ascending:  h=1 -> (fl(1+e), fl(1-e), -1, -1) = (1, 1-e, -1, -1)   [1+e is a tie -> even: 1]
+                  h=2 -> z0 = 1 + (-1) = 0,  z1 = (1-e) - 1 = -e,  z2 = 2,  z3 = fl(2-e) = 2 [tie -> even]
+      descending: the h >= 4 stages copy the block, h=2 -> (0, e, 2, e), h=1 -> z0 = 0 + e = e
+    So z0 is +0 in the ascending order and 2^-24 in the descending one, and its 3-bit code is
+    3 (y = 0 is not above the middle threshold 0) against 4.  The stages h >= 4 combine the first
+    4-block with zero blocks, so the whole output is the 4-point result repeated."""
+    e = np.float32(2.0 ** -24)
+    x = np.zeros(128, np.float32)
+    x[0], x[1], x[2] = 1.0, e, -1.0
+    z = hadamard.fwht_f32(x)
+    want = np.tile(np.array([0.0, -e, 2.0, 2.0], np.float32), 32)
+    assert np.array_equal(z.view(np.uint32), want.view(np.uint32))  # bitwise: +0, not -0 or e
+    n, codes = codec.v_encode(x[None], 3)
+    # n = sqrt(fl(fl(1 + e^2) + 1)) = sqrt(2) rounded = 0x3fb504f3; y2 = y3 = 2 * fl(1/n) ~ 1.4142 -> code 6
+    assert n[0].view(np.uint32) == 0x3FB504F3
+    assert list(codes[0][:4]) == [3, 3, 6, 6] and np.array_equal(codes[0], np.tile(codes[0][:4], 32))
+
+
+def test_v_normalisation_multiplies_by_the_rounded_reciprocal():
+    """Reading: y = z * fl(1/n) (one fp32 division for the reciprocal, then fp32 products), not
+    fl(z / n).  x = (a, b, 0, ...), d = 128, a = 0x3f553488, b = 0x3d2f22b9:
+      a*a = 0x3f319075, b*b = 0x3aefa0fb, sum = 0x3f320845, n = sqrt = 0x3f557c6a
+      z_even = fl(a + b) = 0x3f6026b4,  r = fl(1/n) = 0x3f997d7b
+      z_even * r = 0x3f866500 = 1.049957275390625, which is exactly the 3-bit threshold tau_5
+      fl(z_even / n) = 0x3f866501, one ulp above tau_5
+    With the strict count the product reading gives code 5 (a tie goes to the lower code), the
+    quotient reading code 6.  Odd coordinates: y = fl(a - b) * r = 0.9474 -> code 5."""
+    a, b = _f(0x3F553488), _f(0x3D2F22B9)
+    x = np.zeros(128, np.float32)
+    x[0], x[1] = a, b
+    _, thr = lloyd_max.table_f32(3)
+    assert thr[5].view(np.uint32) == 0x3F866500
+    n, codes = codec.v_encode(x[None], 3)
+    assert n[0].view(np.uint32) == 0x3F557C6A
+    assert np.all(codes[0] == 5)
+
+
+def test_k_quotient_is_a_division_rounded_half_to_even():
+    """Reading: q = rint(fl(k / s)), round half to even, s = fl(amax / 127).
+    amax = 0x40b7c408 (5.742679...), k = 0x4082f381 (4.092224...):
+      s = fl(amax / 127) = 0x3d393675
+      fl(k / s) = 90.5 exactly          -> rint half-even = 90 (half away from zero would give 91)
+      fl(k * fl(1/s)) = 90.50000762...  -> 91 (the reciprocal reading)
+    and -k gives -90 (symmetric)."""
+    amax, k = _f(0x40B7C408), _f(0x4082F381)
+    s, q = codec.k_quantize(np.array([amax, k, -k], np.float32))
+    assert np.float32(s).view(np.uint32) == 0x3D393675
+    assert list(q) == [127, 90, -90]
