@@ -190,6 +190,19 @@ typedef struct {
  * are batched), V is accumulated in the rotated domain and one inverse FWHT
  * is applied per output.  fp32 accumulation.
  *
+ * Query range and precision.  Any finite bf16 or fp32 query is accepted.  The
+ * matrix-core pool kernel and the segment kernel take K codes as exact fp16
+ * values and multiply each query row by an exact power of two 2^-e that
+ * brings its largest element below 2^15 before the fp16 conversion (e > 0
+ * only for rows reaching 2^15; the scores are multiplied back by 2^e), so
+ * large queries neither overflow nor lose precision to an offset; bf16
+ * elements more than 2^39 below their row's largest one fall into fp16's
+ * subnormal range (an absolute error below 2^(e-25) each).  Scores are fp32:
+ * where sigma * q . k reaches ~1e4 nats and keys are tied in their dominant
+ * term, the remainder that breaks the tie is below fp32 resolution and the
+ * outputs can differ from exact attention by more than 1e-3 (so does any fp32
+ * computation of those scores).
+ *
  * workspace: device scratch of *workspace_bytes bytes (256-byte aligned).
  * Call with workspace == NULL to have the required size written to
  * *workspace_bytes (nothing enqueued); PKV_ENOSPACE if the given size is too

@@ -723,9 +723,9 @@ __global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
 // ------------------------------------------------------------------ private segments
 // A private segment (a pool of at most 8 rows: one agent's own older tokens) is decoded
 // by one wavefront per (segment agent, layer, kv head), like the native suffix, with
-// the pool's encoding: scores from int8 K as exact fp16 (1152 + k, the offset removed
-// by starting each lane's sum at -1152 * its query values) against fp16 query pairs
-// (v_dot2_f32_f16); V accumulated in the rotated domain, acc = sum p * Vn * c[code],
+// the pool's encoding: scores from int8 K as exact fp16 against fp16 query pairs
+// (v_dot2_f32_f16; each query row pre-scaled by 2^-e so it fits fp16, the score scaled
+// back by 2^e); V accumulated in the rotated domain, acc = sum p * Vn * c[code],
 // from an fp32 centroid table in LDS.  The result is a partial record (m, l, acc) in
 // the pool kernels' layout (one split), merged by k_merge with the shared pool's.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -736,11 +736,13 @@ __device__ __forceinline__ uint32_t pack_h2f(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 4 int8 codes -> 4 fp16 values 1152 + k (offset byte in the mantissa of 1024), as two pairs
+// 4 int8 codes -> 4 fp16 values k, as two pairs: the byte k + 128 in the mantissa of 1024
+// gives 1024 + (k + 128), and a packed fp16 subtraction of 1152 leaves k (all exact)
 __device__ __forceinline__ void i8x4_to_h2x2(uint32_t w, uint32_t& lo, uint32_t& hi) {
     const uint32_t u = w ^ 0x80808080u;
-    lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-    hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
 }
 
 template <int D, int RS, int BITS>
@@ -780,9 +782,10 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
 
     for (int r0 = 0; r0 < a.G; r0 += RS) {
         const int nr = min(RS, a.G - r0);
-        // query slices as fp16 pairs (dims 16 part .. 16 part + 15) and the offset start
+        // query slices as fp16 pairs (dims 16 part .. 16 part + 15), each row times 2^-e so that
+        // it stays below 2^15 (max|q| < 2^E, e = max(0, E - 15)); qsc = 2^e restores the score
         uint32_t qp[RS][8];
-        float qoff[RS];
+        float qsc[RS];
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
             const int rr = min(r0 + r, a.G - 1);
@@ -801,14 +804,18 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[i] = static_cast<const float*>(a.q)[qo + i];
             }
-            float sum = 0.0f;
+            float mx = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                qp[r][i] = pack_h2f(x[2 * i], x[2 * i + 1]);
-                const half2_t h = __builtin_bit_cast(half2_t, qp[r][i]);
-                sum += (float)h[0] + (float)h[1];
-            }
-            qoff[r] = -1152.0f * sum;
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x[i]));
+#pragma unroll
+            for (int off = 1; off < LPT; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));  // the row's lanes
+            int ex = 0;
+            frexpf(mx, &ex);
+            const int e = ex > 15 ? ex - 15 : 0;
+            qsc[r] = ldexpf(1.0f, e);
+            const float qinv = ldexpf(1.0f, -e);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qp[r][i] = pack_h2f(x[2 * i] * qinv, x[2 * i + 1] * qinv);
         }
         float M[RS], Lp[RS], acc[RS][4];
 #pragma unroll
@@ -855,11 +862,12 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
                     float sc[RS];
 #pragma unroll
                     for (int r = 0; r < RS; ++r) {
-                        sc[r] = qoff[r];
+                        sc[r] = 0.0f;
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
                             sc[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kh[i]),
                                                            __builtin_bit_cast(half2_t, qp[r][i]), sc[r], false);
+                        sc[r] *= qsc[r];
                     }
                     auto red = [&](auto bt) {
                         constexpr int b = decltype(bt)::value;

@@ -12,8 +12,9 @@
 // split); each wavefront streams every 4th 32-token step of the split and
 // keeps all rows (up to 64, in RT tiles of 16) in its accumulators:
 //
-//   S^T[32 tok][16 rows] = (1152 + Kq as exact fp16) x Q^T (fp16), accumulator
-//   started at -1152 * sum(q)                                      2*RT*(d/32) MFMAs
+//   S^T[32 tok][16 rows] = (Kq as exact fp16) x Q'^T (fp16)          2*RT*(d/32) MFMAs
+//   with Q' = Q * 2^-e per row (e > 0 only for rows past the fp16 range; the scores
+//   are multiplied back by 2^e)
 //   x = S * (Ks[t] * sigma * log2 e) - mref with a fixed per-row reference (see
 //   below); w = p * Vn[t] * 2^(7-e) with e from the per-head max norm, so
 //   w < 2^15, split into fp16 hi + lo parts
@@ -131,14 +132,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 4 int8 (two's complement) -> 4 fp16 holding 1152 + k exactly: the bytes u = k + 128
-// are placed in the mantissa of 1024 (fp16 0x6400), giving 1024 + u.  The constant
-// 1152 * sum(q) this adds to every score is subtracted by starting the MFMA
-// accumulator at -1152 * sum(q).
-__device__ __forceinline__ void i8x4_to_h4_offset(uint32_t w, uint32_t& lo, uint32_t& hi) {
+// 4 int8 (two's complement) -> 4 fp16 holding k exactly: the bytes u = k + 128 are
+// placed in the mantissa of 1024 (fp16 0x6400), giving 1024 + u, and one packed fp16
+// subtraction of 1152 leaves u - 128 = k (every step exact: integers below 2048).
+// Exact operands keep the MFMA accumulator at the size of q . k itself, so its fp32
+// rounding does not grow with the query's sum.
+__device__ __forceinline__ void i8x4_to_h4(uint32_t w, uint32_t& lo, uint32_t& hi) {
     const uint32_t u = w ^ 0x80808080u;
-    lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-    hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
 }
 
 // v_max3_f32 without the NaN-quieting the compiler adds around fmaxf of loaded or
@@ -496,15 +499,20 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     for (int it = 0; it < RG::kStages - 1; ++it)
         if (it < my_steps) issue(it);
 
-    // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i);
-    // bf16 values convert exactly (8 significant bits) within fp16's range, fp32
-    // values are split into fp16 hi + lo operands
+    // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i).
+    // Each row is first multiplied by 2^-e, e = max(0, E - 15) with max|q| < 2^E, so every
+    // operand is below 2^15 (fp16 holds up to 65504); the power of two is exact and the
+    // scores are multiplied back by qsc = 2^e.  bf16 values then convert exactly (8
+    // significant bits; only values more than 2^39 below the row's largest reach fp16's
+    // subnormal range), fp32 values are split into fp16 hi + lo operands.
     half8 qreg[RT][KS];  // kept in registers for the whole unit
     half8 qlo[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
-    float qoff[RT];
+    float qsc[RT];
+    bool any_scaled = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        float sum = 0.0f;
+        float xs[KS][8];
+        float mx = 0.0f;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             uint32_t w[8];
@@ -521,29 +529,39 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                     w[2 * i + 1] = h[i] & 0xffff0000u;
                 }
             }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xs[k][i] = rok[rt] ? __uint_as_float(w[i]) : 0.0f;
+                mx = fmaxf(mx, fabsf(xs[k][i]));
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        int ex = 0;
+        frexpf(mx, &ex);  // mx < 2^ex
+        const int e = ex > 15 ? ex - 15 : 0;
+        qsc[rt] = ldexpf(1.0f, e);
+        const float qinv = ldexpf(1.0f, -e);
+        any_scaled |= e > 0;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
             H8 hv, lv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x0 = rok[rt] ? __uint_as_float(w[2 * i]) : 0.0f;
-                const float x1 = rok[rt] ? __uint_as_float(w[2 * i + 1]) : 0.0f;
+                const float x0 = xs[k][2 * i] * qinv, x1 = xs[k][2 * i + 1] * qinv;
                 hv.u[i] = pack_h2(x0, x1);
-                const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
-                sum += (float)hh[0] + (float)hh[1];
                 if constexpr (QSPLIT) {
+                    const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
                     lv.u[i] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
-                    const half2v ll = __builtin_bit_cast(half2v, lv.u[i]);
-                    sum += (float)ll[0] + (float)ll[1];
                 }
             }
             qreg[rt][k] = hv.h;
             asm volatile("" : "+a"(qreg[rt][k]));  // a matrix-core operand only: kept in AGPRs
             if constexpr (QSPLIT) qlo[rt][k] = lv.h;
         }
-        // -1152 * sum of the row's fp16 query values: cancels the offset carried by K
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        qoff[rt] = -1152.0f * sum;
     }
+    // every wavefront of the workgroup holds all rows, so they all take the same branch below
+    const bool scaled_rows = __builtin_amdgcn_ballot_w64(any_scaled) != 0ull;
     if constexpr (BITS == 3) {
         // LUT of fp16 centroid quads: entry e = c0 | c1 << 3 | c2 << 6 | c3 << 9 ->
         // (c[c0], c[c1], c[c2], c[c3]); this thread's entries tid + 256 k share the low pair
@@ -596,7 +614,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         const uint32_t sa = ring_a + (it % RG::kStages) * RG::kStageBytes;
         ring_read<SL::NK, CB>(sa + SL::KOFF + lane * 16, sa + SL::VOFF + lane * SL::VLANE, sa + SL::NOFF + 32 * lg, r);
     };
-    // K as fp16 operands (1152 + k, exact; the offset is removed by the accumulator init)
+    // K as exact fp16 operands
     auto convert_k = [&](const Raw& r, half8 (&ka)[2][KS]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -604,16 +622,22 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             for (int k = 0; k < KS; ++k) {
                 const u32x4 v = r.kr[u * (DL / 16) + k / 2];
                 H8 h;
-                i8x4_to_h4_offset((k & 1) ? v.z : v.x, h.u[0], h.u[1]);
-                i8x4_to_h4_offset((k & 1) ? v.w : v.y, h.u[2], h.u[3]);
+                i8x4_to_h4((k & 1) ? v.z : v.x, h.u[0], h.u[1]);
+                i8x4_to_h4((k & 1) ? v.w : v.y, h.u[2], h.u[3]);
                 ka[u][k] = h.h;
             }
     };
+    float cref[RT], lsum[RT], xmax[RT];
+    f32x4 acc[RT][NB];
+    // the token loop, compiled twice: SCALED multiplies every score tile by its rows' 2^e
+    // (taken only when some row of the unit is past the fp16 range)
+    auto unit_body = [&](auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
     // S^T of row tile rt for the step's 32 tokens: lane (lg, rl) gets tokens
     // 8 lg + 4 u + j of row 16 rt + rl in S[u][j] (q . k for the int8 codes k)
     auto scores = [&](const half8 (&ka)[2][KS], int rt, f32x4 (&S)[2]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) S[u] = f32x4{qoff[rt], qoff[rt], qoff[rt], qoff[rt]};
+        for (int u = 0; u < 2; ++u) S[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         // the two tiles' chains interleaved
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
@@ -622,6 +646,10 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qreg[rt][k], S[u], 0, 0, 0);
                 if constexpr (QSPLIT) S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][k], qlo[rt][k], S[u], 0, 0, 0);
             }
+        }
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) S[u] *= qsc[rt];
         }
     };
     auto norms = [&](const u32x4 (&ns)[4], float (&nn)[8], float (&ff)[8]) {
@@ -641,7 +669,6 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // x = score - mref + lnu, p' = 2^x = p * nu, w = p' * vn.  If a score exceeds
     // mref + kLazy the weights could leave fp16 range: the workgroup then re-runs
     // the unit with the exact row maxima as references.
-    float cref[RT], lsum[RT], xmax[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) cref[rt] = 0.0f;
     if (my_steps > 0) {
@@ -668,7 +695,6 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
     }
 
-    f32x4 acc[RT][NB];
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -783,6 +809,9 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
         lds_barrier();
     }
+    };
+    if (scaled_rows) unit_body(std::true_type{});
+    else unit_body(std::false_type{});
     const float inv_nu = 1.0f / nu;
     float m[RT];
 #pragma unroll

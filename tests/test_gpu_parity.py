@@ -270,3 +270,33 @@ def test_zero_agents_is_a_no_op():
     q = torch.zeros((0, 1, 1, 64), dtype=torch.bfloat16, device=h.DEV)
     out = torch.zeros((0, 1, 1, 64), dtype=torch.float32, device=h.DEV)
     assert pk.agent_decode_attention([], q, out) == 0
+
+
+def test_last_bit_conventions_on_device():
+    """The hand-worked inputs of the oracle's last-bit pins, encoded by the device: K quotient
+    by division rounded half to even (90.5 -> 90), ascending FWHT stage order (a coordinate
+    that is +0 only in that order -> the lower code), V normalised by the rounded reciprocal
+    (a coordinate landing exactly on a threshold -> the lower code).  Expected values are the
+    literals worked out by hand in the oracle's tests."""
+    from oracle import codec
+
+    h = H()
+    print("[quant] last-bit conventions", flush=True)
+    f = lambda b: np.frombuffer(int(b).to_bytes(4, "little"), dtype=np.float32)[0]  # noqa: E731
+    d = 128
+    k = np.zeros((1, 1, 3, d), np.float32)
+    k[0, 0, 0, 0], k[0, 0, 1, 0], k[0, 0, 2, 0] = f(0x40B7C408), f(0x4082F381), -f(0x4082F381)
+    v = np.zeros((1, 1, 3, d), np.float32)
+    v[0, 0, 0, :3] = [1.0, 2.0 ** -24, -1.0]
+    v[0, 0, 1, :2] = [f(0x3F553488), f(0x3D2F22B9)]
+    dp = h.DevicePool(1, 1, d, 32, [3])
+    dp.append(0, torch.from_numpy(k).to(h.DEV), torch.from_numpy(v).to(h.DEV))
+    buf = dp.host_bytes()
+    lay = pool_image.layout(1, 1, d, 32, [3])
+    kq = buf[lay.kq:lay.kq + 32 * d].view(np.int8).reshape(32, d)
+    assert list(kq[:3, 0]) == [127, 90, -90] and not kq[:3, 1:].any()
+    assert list(buf[lay.ks:lay.ks + 12].view(np.uint32)) == [0x3D393675] * 3
+    assert list(buf[lay.vn:lay.vn + 12].view(np.uint32)) == [0x3FB504F3, 0x3F557C6A, 0]
+    codes = codec.unpack_codes(buf[lay.vc[0]:lay.vc[1]].reshape(4, d * 3), d, 3)
+    assert np.array_equal(codes[0], np.tile(np.array([3, 3, 6, 6], np.uint8), 32))
+    assert np.all(codes[1] == 5) and np.all(codes[2] == 0)
