@@ -1243,8 +1243,7 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
                 e.seg_begin = L.seg_units;
                 L.seg_units += (int)agents.size() * units;
             }
-            e.part_off = part;
-            part += (uint64_t)units * e.splits * e.rows * record_floats(d);
+            e.part_off = 0;  // assigned below, once the launch is known to finish its rows in the pool kernel or not
             if (!seg) wg += units * e.splits * e.rblocks;
             e.agent_base = agents[0];
             for (size_t i = 0; i < agents.size(); ++i)
@@ -1289,6 +1288,21 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             ++ci;
         }
         L.n_agents = n_agents;
+        // The matrix-core kernel finishes the rows itself when every pool has one split and every
+        // private pool is a segment (whose records k_seg writes); then only segments and suffixes
+        // need partial records in the workspace, otherwise every pool does (read by k_merge).
+        L.fused = use_mfma ? 1 : 0;
+        for (int p = 0; p < L.n_pools; ++p)
+            if (L.pools[p].seg_begin < 0 && L.pools[p].splits != 1) L.fused = 0;
+        for (int k = 0; k < L.n_agents; ++k)
+            if (L.agent_pool2[k] >= 0 && L.pools[L.agent_pool2[k]].seg_begin < 0) L.fused = 0;
+        const int units = x->layer_count * hkv;
+        for (int p = 0; p < L.n_pools; ++p) {
+            PoolEntry& e = L.pools[p];
+            if (L.fused && e.seg_begin < 0) continue;
+            e.part_off = part;
+            part += (uint64_t)units * e.splits * e.rows * record_floats(d);
+        }
         if (L.has_sfx) {
             L.sfx_part_off = part;
             part += (uint64_t)n_agents * x->layer_count * x->n_q_heads * record_floats(d);
@@ -1390,13 +1404,8 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         }
         if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
-            // one split per (pool, layer, kv head): the MFMA kernel finishes the rows itself
-            // one split per (pool, layer, kv head) and every private pool a segment (its records
-            // written by k_seg above): the MFMA kernel finishes the rows itself
-            L.fused = 1;
-            for (int p = 0; p < L.n_pools; ++p) L.fused &= L.pools[p].splits == 1;
-            for (int k = 0; k < L.n_agents; ++k)
-                if (L.agent_pool2[k] >= 0 && L.pools[L.agent_pool2[k]].seg_begin < 0) L.fused = 0;
+            // L.fused (set by the plan): one split per (pool, layer, kv head) and every private pool
+            // a segment, so the MFMA kernel finishes the rows itself
             const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
             if (st != PKV_OK) return st;
         } else {
@@ -1416,14 +1425,17 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
 }  // namespace
 }  // namespace pkv
 
-extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
-                                      void* stream) {
-    using namespace pkv;
-    if (!workspace_bytes) return PKV_EINVAL;
+namespace pkv {
+namespace {
+
+// Validation, kernel choice and launch plan shared by both decode entry points.  Returns
+// PKV_OK with *empty set for a call with no work.
+int prepare(const pkv_decode_args* args, Plan* plan, bool* use_mfma, bool* empty) {
+    *empty = false;
     const int v = validate(args);
     if (v != PKV_OK) return v;
     if (args->n_agents == 0 || args->layer_count == 0) {
-        if (!workspace) *workspace_bytes = 0;
+        *empty = true;
         return PKV_OK;
     }
     // rows per pool (agents of the pool times the GQA group) decide which pool kernel can run
@@ -1440,9 +1452,33 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
     // fp32 queries need hi + lo query operands; above 48 rows they do not fit the registers
     const bool mfma_ok = max_rows <= (args->q_dtype == PKV_F32 ? 48 : 64);
     if (args->kernel == PKV_KERNEL_MFMA && !mfma_ok) return PKV_EUNSUPPORTED;
-    const bool use_mfma = args->kernel == PKV_KERNEL_MFMA || (args->kernel == PKV_KERNEL_DEFAULT && mfma_ok);
+    *use_mfma = args->kernel == PKV_KERNEL_MFMA || (args->kernel == PKV_KERNEL_DEFAULT && mfma_ok);
+    make_plan(args, *use_mfma, plan);
+    if (args->pool_events && (!args->pool_events[0] || !args->pool_events[1])) return PKV_EINVAL;
+    return PKV_OK;
+}
+
+int enqueue_plan(const pkv_decode_args* args, const Plan& plan, bool use_mfma, float* ws, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (args->agent_pool[0]->cfg.head_dim == 128) return enqueue<128>(plan, use_mfma, ws, args->pool_events, s);
+    return enqueue<64>(plan, use_mfma, ws, args->pool_events, s);
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
+                                      void* stream) {
+    using namespace pkv;
+    if (!workspace_bytes) return PKV_EINVAL;
     Plan plan;
-    make_plan(args, use_mfma, &plan);
+    bool use_mfma = false, empty = false;
+    const int st = prepare(args, &plan, &use_mfma, &empty);
+    if (st != PKV_OK) return st;
+    if (empty) {
+        if (!workspace) *workspace_bytes = 0;
+        return PKV_OK;
+    }
     const size_t need = plan.ws_floats * sizeof(float);
     if (!workspace) {
         *workspace_bytes = need;
@@ -1450,9 +1486,5 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
     }
     if (*workspace_bytes < need) return PKV_ENOSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return PKV_EINVAL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float* ws = static_cast<float*>(workspace);
-    if (args->pool_events && (!args->pool_events[0] || !args->pool_events[1])) return PKV_EINVAL;
-    if (args->agent_pool[0]->cfg.head_dim == 128) return enqueue<128>(plan, use_mfma, ws, args->pool_events, s);
-    return enqueue<64>(plan, use_mfma, ws, args->pool_events, s);
+    return enqueue_plan(args, plan, use_mfma, static_cast<float*>(workspace), stream);
 }
