@@ -216,6 +216,28 @@ typedef struct {
 int agent_decode_attention(const pkv_decode_args* args, void* workspace, size_t* workspace_bytes,
                            void* stream);
 
+/*
+ * agent_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same kernels and launch plan run,
+ * with their partial records in a fixed device array of the library instead
+ * of the workspace: pkv_noalloc_scratch_bytes() bytes (32 MiB), one copy per
+ * device, held until the process ends.  Nothing is allocated by the call.
+ *
+ * Limit: a call whose workspace (the size agent_decode_attention reports)
+ * exceeds the array returns PKV_ENOSPACE before anything is enqueued.  The
+ * array keeps the previous call's contents; no kernel reads a record it has
+ * not written in the same call, so nothing needs clearing.  Every call on one
+ * device shares that device's array: calls that may overlap on one device
+ * (different streams, or different host threads without ordering) race and
+ * must be serialised by the caller.  Errors as agent_decode_attention, plus
+ * PKV_EHIP if the array's device address cannot be obtained.
+ */
+int agent_decode_attention_noalloc(const pkv_decode_args* args, void* stream);
+
+/* Bytes of the per-device array agent_decode_attention_noalloc uses. */
+size_t pkv_noalloc_scratch_bytes(void);
+
 /* ---- handing a pool over, and kv-head shards ---- */
 
 /* Header of a pool image handed to another buffer, process or device: with the

@@ -21,6 +21,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <vector>
 
 #include "pkv_decode.h"
@@ -1487,4 +1488,50 @@ extern "C" int agent_decode_attention(const pkv_decode_args* args, void* workspa
     if (*workspace_bytes < need) return PKV_ENOSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return PKV_EINVAL;
     return enqueue_plan(args, plan, use_mfma, static_cast<float*>(workspace), stream);
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// The decode kernels' workspace (suffix, segment and split partial records) in a fixed device
+// array instead of a caller buffer, for callers that cannot allocate (graph capture, tight
+// serving loops).  Each device holds its own copy of the array until the process ends.  Host
+// code never uses the array's name as an address: its device address is fetched once per device
+// with hipGetSymbolAddress (with that device current) and kept in scratch_dev[].
+static constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace pkv {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // device address of `scratch` per device, nullptr until fetched
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return PKV_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_EHIP;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return PKV_OK;
+}
+}  // namespace
+}  // namespace pkv
+
+extern "C" size_t pkv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int agent_decode_attention_noalloc(const pkv_decode_args* args, void* stream) {
+    using namespace pkv;
+    Plan plan;
+    bool use_mfma = false, empty = false;
+    const int st = prepare(args, &plan, &use_mfma, &empty);
+    if (st != PKV_OK || empty) return st;
+    if (plan.ws_floats * sizeof(float) > kScratchBytes) return PKV_ENOSPACE;
+    void* ws = nullptr;
+    const int sa = scratch_address(&ws);
+    if (sa != PKV_OK) return sa;
+    return enqueue_plan(args, plan, use_mfma, static_cast<float*>(ws), stream);
 }

@@ -159,7 +159,7 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 104; }
+int pkv_version(void) { return 105; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {

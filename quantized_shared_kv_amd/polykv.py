@@ -14,7 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
-ABI_VERSION = 104  # pkv_version() of the library these ctypes mirrors describe
+ABI_VERSION = 105  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.pool_quantize_append.restype = c_int32
         L.agent_decode_attention.argtypes = [POINTER(DecodeArgs), c_void_p, POINTER(c_size_t), c_void_p]
         L.agent_decode_attention.restype = c_int32
+        L.agent_decode_attention_noalloc.argtypes = [POINTER(DecodeArgs), c_void_p]
+        L.agent_decode_attention_noalloc.restype = c_int32
+        L.pkv_noalloc_scratch_bytes.restype = c_size_t
         L.pkv_strerror.argtypes = [c_int32]
         L.pkv_strerror.restype = ctypes.c_char_p
         L.pkv_version.restype = c_int32
@@ -253,6 +256,23 @@ def agent_decode_attention(pools, q, out, layer_begin=0, sfx_k=None, sfx_v=None,
                                         c_void_p(_stream_handle(stream))), "agent_decode_attention")
     del keep
     return int(size.value)
+
+
+def agent_decode_attention_noalloc(pools, q, out, layer_begin=0, sfx_k=None, sfx_v=None, sfx_len=None,
+                                   softmax_scale=0.0, kernel=KERNEL_DEFAULT, splits=0, stream=None,
+                                   pool_events=None, private_pools=None) -> None:
+    """Enqueue one decode call whose partial records use the library's per-device scratch array
+    (no workspace, nothing allocated).  Arguments as agent_decode_attention."""
+    a, keep = _decode_args(pools, q, out, layer_begin, sfx_k, sfx_v, sfx_len, softmax_scale, kernel, splits,
+                           pool_events, private_pools)
+    _check(lib().agent_decode_attention_noalloc(ctypes.byref(a), c_void_p(_stream_handle(stream))),
+           "agent_decode_attention_noalloc")
+    del keep
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-device array agent_decode_attention_noalloc uses."""
+    return int(lib().pkv_noalloc_scratch_bytes())
 
 
 def lloyd_max_table(bits: int):
