@@ -153,14 +153,17 @@ typedef struct {
     int32_t sfx_cap;                  /* suffix capacity per agent (>= max sfx_len) */
     const int32_t* sfx_len;           /* host [n_agents]: native tokens agent a attends to; may be NULL (all 0) */
     float* out;                       /* device fp32 [n_agents][layer_count][n_q_heads][head_dim] */
-    int32_t kernel;                   /* pool kernel: PKV_KERNEL_DEFAULT (MFMA when every pool has
-                                         at most 64 rows = agents * q heads per kv head, 48 with fp32
-                                         queries, else VALU), PKV_KERNEL_VALU, or PKV_KERNEL_MFMA
-                                         (PKV_EUNSUPPORTED above those row counts) */
+    int32_t kernel;                   /* pool kernel: PKV_KERNEL_DEFAULT or PKV_KERNEL_MFMA (the
+                                         matrix-core kernel for any number of rows = agents * q heads
+                                         per kv head: a pool with more than 64 rows, 48 with fp32
+                                         queries, runs in balanced row blocks of at most that many, one
+                                         workgroup each, the blocks of one (layer, kv head) on one XCD),
+                                         or PKV_KERNEL_VALU (the fp32 vector kernel) */
     int32_t splits;                   /* token splits per (pool, layer, kv head); 0 = automatic */
     void* const* pool_events;         /* optional instrumentation: NULL, or two hipEvent_t recorded on
-                                         the stream right before the first and right after the last
-                                         pool-kernel launch of the call */
+                                         the stream right before the first compressed-pool kernel
+                                         (private segments, then the pool kernel) and right after the
+                                         last pool-kernel launch of the call */
     const pkv_pool* const* agent_private_pool;
                                       /* optional, host [n_agents]: NULL, or per agent NULL or a second
                                          pool the agent alone (or every agent naming it) also attends:
@@ -336,6 +339,22 @@ int comix_sensitivity(const pkv_comix_args* args, void* stream);
  */
 int comix_allocate_bits(int32_t n_items, const float* sensitivity, const uint64_t* cost,
                         const double* error_factor, uint64_t budget, uint8_t* bits);
+
+/* ---- measurement aid ---- */
+
+/*
+ * Read `bytes` bytes of device memory at src (16-byte aligned, bytes a multiple
+ * of 16) with a plain streaming kernel and write the XOR of every 32-bit word,
+ * folded per wavefront, to sink (device, pkv_stream_read_sink_words() words; the
+ * XOR of all of them is the XOR of the buffer's words).  Not part of the decode
+ * path: its time over a buffer far larger than the last-level cache is the
+ * practical HBM read ceiling that the decode kernels' bandwidth is compared
+ * with.  Errors: PKV_EINVAL, PKV_EHIP.
+ */
+int pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/* Words of the sink pkv_stream_read writes. */
+size_t pkv_stream_read_sink_words(void);
 
 /* ---- auxiliary queries (host only, no device work) ---- */
 

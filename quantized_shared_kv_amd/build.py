@@ -23,7 +23,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 OBJ_DIR = os.path.join(OUT_DIR, "obj")
 LIB = os.path.join(OUT_DIR, "libpolykv.so")
 SOURCES = ["pkv_host.cpp", "pkv_quantize.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_comix.hip",
-           "pkv_handoff.cpp"]
+           "pkv_handoff.cpp", "pkv_stream.hip"]
 ARCH = "gfx950"
 
 

@@ -24,6 +24,7 @@ struct PoolEntry {
     int32_t splits;        // token splits per (layer, kv head)
     int32_t chunk;         // tokens per split (multiple of 32)
     int32_t rblocks;       // row blocks per (layer, kv head, split)
+    int32_t rb_rows;       // rows per row block (the last block may hold fewer)
     int32_t wg_begin;      // first workgroup of this pool in the launch
     int32_t seg_begin;     // >= 0: a private segment decoded by k_seg (no pool-kernel workgroups),
                            // its first unit there; -1: decoded by the pool kernel
@@ -72,11 +73,25 @@ __device__ inline int layer_bits_prefix(const PoolEntry& p, int l) {
     return acc;
 }
 
+// Matrix-core kernel: the pool-local workgroup index w -> (item, row block), item = (layer,
+// kv head, split) in split-fastest order.  The row blocks of one item sit 8 workgroups apart, so
+// with workgroups dealt to the 8 XCDs in turn they share an XCD (and its L2) when the pool's
+// start is a multiple of 8; with one row block this is the identity.
+__host__ __device__ inline int pool_item_of_wg(int w, int items, int rblocks, int* rb) {
+    if (rblocks == 1) {
+        *rb = 0;
+        return w;
+    }
+    const int grp = w / (8 * rblocks), within = w % (8 * rblocks);
+    const int cnt = items - grp * 8 < 8 ? items - grp * 8 : 8;
+    *rb = within / cnt;
+    return grp * 8 + within % cnt;
+}
+
 // Records of partial softmax state: [m (log2 units), l, acc[d]].
 inline int record_floats(int d) { return 2 + d; }
 
 // Launches implemented in pkv_decode_mfma.hip.
 int launch_pool_mfma(const DecodeLaunch& a, int total_wg, hipStream_t s);
-bool mfma_supported(const DecodeLaunch& a);
 
 }  // namespace pkv

@@ -1226,21 +1226,26 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.agent0 = agent0;
             const int units = x->layer_count * hkv;
             const int tiles = std::max(1, (e.T + kTile - 1) / kTile);
+            // row blocks: the matrix-core kernel holds at most 64 rows per workgroup (48 with fp32
+            // queries), balanced over the blocks; the vector kernel 32
+            const int block_max = use_mfma ? (x->q_dtype == PKV_F32 ? 48 : 64) : kValuRows;
+            e.rblocks = (e.rows + block_max - 1) / block_max;
+            e.rb_rows = use_mfma ? (e.rows + e.rblocks - 1) / e.rblocks : kValuRows;
             int splits = x->splits;
             // default split: enough workgroups to cover the 256 compute units (MFMA: one
             // 4-wave workgroup per CU; VALU: two per CU)
             const int target = use_mfma ? 256 : 512;
-            if (splits <= 0) splits = std::max(1, std::min(tiles, (target + units - 1) / units));
+            if (splits <= 0) splits = std::max(1, std::min(tiles, (target + units * e.rblocks - 1) / (units * e.rblocks)));
             splits = std::min(splits, tiles);
             e.chunk = (tiles + splits - 1) / splits * kTile;
             e.splits = std::max(1, (std::max(e.T, 1) + e.chunk - 1) / e.chunk);
-            e.rblocks = use_mfma ? 1 : (e.rows + kValuRows - 1) / kValuRows;
             e.wg_begin = wg;
             e.seg_begin = -1;
             if (seg) {
                 e.splits = 1;
                 e.chunk = std::max(e.T, 1);
                 e.rblocks = 1;
+                e.rb_rows = e.rows;
                 e.seg_begin = L.seg_units;
                 L.seg_units += (int)agents.size() * units;
             }
@@ -1396,6 +1401,8 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
                 hipLaunchKernelGGL(k_sfx<D>, grid, dim3(kThreads), 0, s, L);
             }
         }
+        // the event pair brackets the compressed-pool work of the call: private segments and the pool kernel
+        if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (L.seg_units > 0) {
             const dim3 grid((L.seg_units + 3) / 4);
             if (L.G == 1) hipLaunchKernelGGL((k_seg<D, 1>), grid, dim3(kThreads), 0, s, L, cents);
@@ -1403,7 +1410,6 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
             else if (L.G <= 4) hipLaunchKernelGGL((k_seg<D, 4>), grid, dim3(kThreads), 0, s, L, cents);
             else hipLaunchKernelGGL((k_seg<D, 8>), grid, dim3(kThreads), 0, s, L, cents);
         }
-        if (events && i == 0 && hipEventRecord(static_cast<hipEvent_t>(events[0]), s) != hipSuccess) return PKV_EHIP;
         if (use_mfma) {
             // L.fused (set by the plan): one split per (pool, layer, kv head) and every private pool
             // a segment, so the MFMA kernel finishes the rows itself
@@ -1439,21 +1445,9 @@ int prepare(const pkv_decode_args* args, Plan* plan, bool* use_mfma, bool* empty
         *empty = true;
         return PKV_OK;
     }
-    // rows per pool (agents of the pool times the GQA group) decide which pool kernel can run
-    int max_rows = 0;
-    {
-        std::map<const pkv_pool*, int> cnt;
-        for (int a = 0; a < args->n_agents; ++a) {
-            max_rows = std::max(max_rows, ++cnt[args->agent_pool[a]]);
-            const pkv_pool* q = args->agent_private_pool ? args->agent_private_pool[a] : nullptr;
-            if (q) max_rows = std::max(max_rows, ++cnt[q]);
-        }
-        max_rows *= args->n_q_heads / args->agent_pool[0]->cfg.n_kv_heads;
-    }
-    // fp32 queries need hi + lo query operands; above 48 rows they do not fit the registers
-    const bool mfma_ok = max_rows <= (args->q_dtype == PKV_F32 ? 48 : 64);
-    if (args->kernel == PKV_KERNEL_MFMA && !mfma_ok) return PKV_EUNSUPPORTED;
-    *use_mfma = args->kernel == PKV_KERNEL_MFMA || (args->kernel == PKV_KERNEL_DEFAULT && mfma_ok);
+    // the matrix-core kernel takes any number of rows per pool (in row blocks of at most 64, 48
+    // with fp32 queries); the vector kernel runs only when asked for
+    *use_mfma = args->kernel != PKV_KERNEL_VALU;
     make_plan(args, *use_mfma, plan);
     if (args->pool_events && (!args->pool_events[0] || !args->pool_events[1])) return PKV_EINVAL;
     return PKV_OK;

@@ -384,13 +384,17 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 
     const int p = find_pool_m(a, blockIdx.x);
     const PoolEntry& P = a.pools[p];
-    int local = blockIdx.x - P.wg_begin;
+    int rb = 0;
+    int local = pool_item_of_wg(blockIdx.x - P.wg_begin, a.lc * a.hkv * P.splits, P.rblocks, &rb);
     const int sp = local % P.splits;
     local /= P.splits;
     const int g = local % a.hkv;
     const int lj = local / a.hkv;
     const int l = a.l0 + lj;
-    const int R = P.rows;
+    // this workgroup's rows: pool rows r0 .. r0 + R - 1 (row block rb); row indices below are
+    // local (LDS tiles, lanes) unless added to r0
+    const int r0 = rb * P.rb_rows;
+    const int R = min(P.rb_rows, P.rows - r0);
 
     const int8_t* kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
     const float* vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
@@ -467,7 +471,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     for (int rt = 0; rt < RT; ++rt) {
         const int rho = 16 * rt + rl;
         rok[rt] = rho < R;
-        const int rr = rok[rt] ? rho : 0;
+        const int rr = r0 + (rok[rt] ? rho : 0);        // pool row
         const int ka = (int)(((float)rr + 0.5f) * rG);  // rr / G, exact for rows < 2^20
         q_agent[rt] = P.agent0 + ka;
         q_head[rt] = g * a.G + rr - ka * a.G;
@@ -837,9 +841,10 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
             const int row = min(wave + kWaves * (4 * i + fq), R - 1);  // rows past R: computed, not stored
-            const int ka = (int)(((float)row + 0.5f) * rG);  // row / G, exact for rows < 2^20
+            const int prow = r0 + row;                                  // pool row
+            const int ka = (int)(((float)prow + 0.5f) * rG);  // prow / G, exact for rows < 2^20
             f_row[i] = row;
-            f_head[i] = g * a.G + row - ka * a.G;
+            f_head[i] = g * a.G + prow - ka * a.G;
             f_agent[i] = P.agent_base >= 0 ? P.agent_base + ka : a.agent_id[P.agent0 + ka];
             su_m[i] = -INFINITY;
             su_l[i] = 0.0f;
@@ -907,7 +912,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
     };
     if (!fused) {
-        float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.splits + sp) * (uint64_t)R * (2 + D);
+        float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.splits + sp) * (uint64_t)P.rows * (2 + D) +
+                      (uint64_t)r0 * (2 + D);
         for (int row = wave; row < R; row += kWaves) {
             float al[kWaves], M, L;
             row_weights(row, al, M, L);
@@ -1013,7 +1019,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 template <int D, int RT, bool QSPLIT>
 __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents) {
     const PoolEntry& P = a.pools[find_pool_m(a, blockIdx.x)];
-    int local = blockIdx.x - P.wg_begin;
+    int rb = 0;
+    int local = pool_item_of_wg(blockIdx.x - P.wg_begin, a.lc * a.hkv * P.splits, P.rblocks, &rb);
     local /= P.splits;
     const int l = a.l0 + local / a.hkv;
     switch (layer_bits(P, l)) {
@@ -1040,17 +1047,13 @@ int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int
 
 }  // namespace
 
-bool mfma_supported(const DecodeLaunch& a) {
-    const int limit = a.q_dtype == PKV_F32 ? 48 : 64;
-    for (int p = 0; p < a.n_pools; ++p)
-        if (a.pools[p].rows > limit) return false;
-    return true;
-}
-
 int launch_pool_mfma(const DecodeLaunch& a, int total_wg, hipStream_t s) {
-    if (!mfma_supported(a)) return PKV_EUNSUPPORTED;
+    // rows per workgroup: the largest row block of the launch's pools (the plan keeps blocks at
+    // most 64 rows, 48 with fp32 queries, whose hi + lo operands take twice the registers)
     int rows = 1;
-    for (int p = 0; p < a.n_pools; ++p) rows = rows > a.pools[p].rows ? rows : a.pools[p].rows;
+    for (int p = 0; p < a.n_pools; ++p)
+        if (a.pools[p].seg_begin < 0) rows = rows > a.pools[p].rb_rows ? rows : a.pools[p].rb_rows;
+    if (rows > (a.q_dtype == PKV_F32 ? 48 : kMaxRows)) return PKV_EUNSUPPORTED;
     const int rt = (rows + 15) / 16;
     CentArg c;
     std::memcpy(c.c, codebook_tables().cent, sizeof(c.c));

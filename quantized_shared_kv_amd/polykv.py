@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.agent_decode_attention_noalloc.argtypes = [POINTER(DecodeArgs), c_void_p]
         L.agent_decode_attention_noalloc.restype = c_int32
         L.pkv_noalloc_scratch_bytes.restype = c_size_t
+        L.pkv_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+        L.pkv_stream_read.restype = c_int32
+        L.pkv_stream_read_sink_words.restype = c_size_t
         L.pkv_strerror.argtypes = [c_int32]
         L.pkv_strerror.restype = ctypes.c_char_p
         L.pkv_version.restype = c_int32
@@ -273,6 +276,20 @@ def agent_decode_attention_noalloc(pools, q, out, layer_begin=0, sfx_k=None, sfx
 def noalloc_scratch_bytes() -> int:
     """Bytes of the per-device array agent_decode_attention_noalloc uses."""
     return int(lib().pkv_noalloc_scratch_bytes())
+
+
+def stream_read(src, sink, stream=None) -> None:
+    """Enqueue the streaming read of the device tensor src (its bytes) into sink (device int32/uint32,
+    at least stream_read_sink_words() elements): the HBM read ceiling of the measurements."""
+    if not (src.is_cuda and sink.is_cuda and src.is_contiguous()) or sink.element_size() != 4 or \
+            sink.numel() < stream_read_sink_words():
+        raise ValueError("src: contiguous device tensor; sink: device 32-bit tensor of stream_read_sink_words()")
+    _check(lib().pkv_stream_read(c_void_p(src.data_ptr()), src.numel() * src.element_size(), c_void_p(sink.data_ptr()),
+                                 c_void_p(_stream_handle(stream))), "pkv_stream_read")
+
+
+def stream_read_sink_words() -> int:
+    return int(lib().pkv_stream_read_sink_words())
 
 
 def lloyd_max_table(bits: int):

@@ -310,3 +310,15 @@ class _FakeWs:
 
     def element_size(self):
         return 1
+
+
+def test_stream_read_validation_is_host_side():
+    """The streaming-read measurement kernel rejects bad arguments before any launch."""
+    lib = pk.lib()
+    f = lib.pkv_stream_read
+    sink = ctypes.c_void_p(1 << 24)
+    assert f(None, 16, sink, None) == -1
+    assert f(ctypes.c_void_p(1 << 20), 16, None, None) == -1
+    assert f(ctypes.c_void_p((1 << 20) + 8), 16, sink, None) == -1   # src not 16-byte aligned
+    assert f(ctypes.c_void_p(1 << 20), 24, sink, None) == -1          # bytes not a multiple of 16
+    assert lib.pkv_stream_read_sink_words() > 0

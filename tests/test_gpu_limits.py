@@ -94,3 +94,23 @@ def test_explicit_softmax_scale(kernel, scale):
     torch.cuda.synchronize()
     want = att.decode_call(q32, [0] * 3, lambda p, l, g: ref.decoded_layer(l, g), fk, fv, lens, 2, sigma=scale)
     assert att.max_rel_error(out.cpu().numpy().astype(np.float64), want) <= TOL
+
+
+def test_stream_read_folds_every_word():
+    """The streaming-read kernel (the measurements' HBM read ceiling) reads every word: the XOR of its
+    per-wavefront results equals the XOR of the buffer's 32-bit words, for sizes that are and are not
+    multiples of the grid's stride."""
+    import numpy as np
+    import torch
+
+    from quantized_shared_kv_amd import polykv as pk
+
+    rng = np.random.default_rng(4)
+    for n in (4, 4 * 1000003, 1 << 22):
+        host = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+        src = torch.from_numpy(host.view(np.int32)).cuda()
+        sink = torch.zeros(pk.stream_read_sink_words(), dtype=torch.int32, device="cuda")
+        pk.stream_read(src, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), n
