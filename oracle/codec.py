@@ -58,16 +58,63 @@ def k_quantize(k: np.ndarray) -> tuple[np.float32, np.ndarray]:
     return s, q
 
 
+def k_quantize_per_token(k: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token int8 quantisation of K vectors (last axis = head_dim): one scale per vector.
+
+    A codec variant measured as an ablation (QKVShare blog, section 3.2, weighs per-tensor
+    against per-token and per-channel granularity; PolyKV explainer, section 2.B, names only
+    the per-tensor scale).  The q8_0 rule of ``k_quantize`` applied to each vector alone:
+    s_t = fl(amax_t / 127) with amax_t = max_i |k_t,i|, q = clamp(rint(fl(k / s_t)), -127, 127),
+    a zero vector gives s_t = 0 and codes 0.  Returns (scales [...], codes int8 [..., d]).
+    """
+    k = np.asarray(k, dtype=np.float32)
+    amax = np.max(np.abs(k), axis=-1) if k.shape[-1] else np.zeros(k.shape[:-1], np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    nz = s > 0
+    q = np.zeros(k.shape, dtype=np.float32)
+    q[nz] = np.rint(k[nz] / s[nz][..., None])
+    return s, np.clip(q, -127.0, 127.0).astype(np.int8)
+
+
+def k_channel_scales(k: np.ndarray) -> np.ndarray:
+    """Per-channel K scales of one block [..., T, d]: s_c = fl(max_t |k_t,c| / 127), shape [..., d]."""
+    k = np.asarray(k, dtype=np.float32)
+    amax = np.max(np.abs(k), axis=-2) if k.shape[-2] else np.zeros(k.shape[:-2] + k.shape[-1:], np.float32)
+    return (amax / np.float32(127.0)).astype(np.float32)
+
+
+def k_quantize_per_channel(k: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """int8 codes of K [..., T, d] under given per-channel scales [..., d] (a codec variant).
+
+    q = clamp(rint(fl(k / s_c)), -127, 127); a channel with s_c = 0 gives codes 0.  The scales
+    of a pool are taken from its first append (``k_channel_scales``) and kept: later tokens
+    are coded with them and clamp at +-127, since stored codes are never re-quantised (CoMixKV
+    news article, "incremental quantization strategy").
+    """
+    k = np.asarray(k, dtype=np.float32)
+    s = np.broadcast_to(np.asarray(scales, dtype=np.float32)[..., None, :], k.shape)
+    q = np.zeros(k.shape, dtype=np.float32)
+    nz = s > 0
+    q[nz] = np.rint(k[nz] / s[nz])
+    return np.clip(q, -127.0, 127.0).astype(np.int8)
+
+
 def k_dequantize(scale, q: np.ndarray) -> np.ndarray:
     """k_hat = scale * q, exact in fp64."""
     return np.float64(scale) * np.asarray(q, dtype=np.float64)
 
 
 # ---------------------------------------------------------------- V codec
-def v_encode(v: np.ndarray, bits: int, signs: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+def v_encode(v: np.ndarray, bits: int, signs: np.ndarray | None = None,
+             corrected_norm: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """Encode V vectors (last axis = head_dim) to (norms fp32, codes uint8).
 
     signs: optional [d] array of +1 / -1 applied to each vector before the FWHT.
+    corrected_norm: store n' = ||v|| sqrt(d) / ||c_hat|| instead of ||v|| (a codec variant
+    measured as an ablation), so that the decoded vector (n'/d) H c_hat has exactly the input's
+    norm (||H c|| = sqrt(d) ||c||).  In fp32: cn = sqrt of the centroids' squares summed by
+    the same halving tree as the norm, n' = fl(fl(n * fl(sqrt(d))) / cn); the codes are the
+    plain codec's (found with 1/||v||); a zero vector keeps n' = 0.
     """
     x = np.asarray(v, dtype=np.float32)
     _, thr = lloyd_max.table_f32(bits)
@@ -83,6 +130,12 @@ def v_encode(v: np.ndarray, bits: int, signs: np.ndarray | None = None) -> tuple
     for t in thr:
         codes += (y > t).astype(np.uint8)
     codes[~nz] = 0
+    if corrected_norm:
+        cent, _ = lloyd_max.table_f32(bits)
+        cn = hadamard.norm_f32(cent[codes])
+        sd = np.float32(np.sqrt(np.float64(x.shape[-1])))
+        n = ((n * sd).astype(np.float32) / cn).astype(np.float32)
+        n[~nz] = 0.0
     return n, codes
 
 

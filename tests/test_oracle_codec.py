@@ -269,3 +269,78 @@ def test_k_quotient_is_a_division_rounded_half_to_even():
     s, q = codec.k_quantize(np.array([amax, k, -k], np.float32))
     assert np.float32(s).view(np.uint32) == 0x3D393675
     assert list(q) == [127, 90, -90]
+
+
+# ---- codec variants (ablations): K per token, K per channel, corrected V norm ----------------------
+
+def test_k_per_token_hand_worked():
+    """One scale per K vector, the q8_0 rule on each vector alone.  Row 0: amax 254 -> s = 2,
+    codes 254/2 = 127, 1/2 = 0.5 -> 0 (half to even), -127/2 = -63.5 -> -64, 0.5/2 -> 0.
+    Row 1: the hand-worked division pin (90.5 -> 90).  Row 2: zeros -> s = 0, codes 0."""
+    k = np.zeros((3, 4), np.float32)
+    k[0] = [254.0, 1.0, -127.0, 0.5]
+    k[1, :2] = [_f(0x40B7C408), _f(0x4082F381)]
+    s, q = codec.k_quantize_per_token(k)
+    assert s[0] == 2.0 and s[1].view(np.uint32) == 0x3D393675 and s[2] == 0.0
+    assert q.tolist() == [[127, 0, -64, 0], [127, 90, 0, 0], [0, 0, 0, 0]]
+
+
+def test_k_per_token_bounds():
+    rng = np.random.default_rng(7)
+    k = (rng.standard_normal((50, 128)) * rng.lognormal(0, 1, (50, 1))).astype(np.float32)
+    s, q = codec.k_quantize_per_token(k)
+    top = np.argmax(np.abs(k), axis=-1)
+    assert np.all(np.abs(q[np.arange(50), top]) == 127)
+    err = np.abs(k.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+
+
+def test_k_per_channel_hand_worked_and_later_appends_clamp():
+    """Channel 0: [127, -63.5, 1.5] -> s = 1, codes 127, -64 (half to even), 2; channel 1 all zero
+    -> s = 0, codes 0.  A later block keeps the first block's scales: 300 clamps to 127, and the
+    zero-scale channel stays 0 whatever its values (stored codes are never re-quantised)."""
+    k = np.array([[127.0, 0.0], [-63.5, 0.0], [1.5, 0.0]], np.float32)
+    s = codec.k_channel_scales(k)
+    assert s.tolist() == [1.0, 0.0]
+    assert codec.k_quantize_per_channel(k, s).tolist() == [[127, 0], [-64, 0], [2, 0]]
+    later = np.array([[300.0, 5.0], [-2.5, -7.0]], np.float32)
+    assert codec.k_quantize_per_channel(later, s).tolist() == [[127, 0], [-2, 0]]
+
+
+def test_corrected_norm_reconstructs_a_basis_vector_exactly():
+    """v = e_0: H v is the all-ones vector, y = 1 everywhere, the 3-bit code of 1 is 5 (between
+    the thresholds 0.5005 and 1.04996), so c_hat = c_5 * ones and ||c_hat|| = sqrt(d) c_5.  The
+    plain norm decodes to (1/d) H (c_5 ones) = c_5 e_0 (shrunk to 0.756); the corrected norm
+    n' = sqrt(d) / (sqrt(d) c_5) = 1 / c_5 decodes to e_0 itself."""
+    cent, _ = lloyd_max.table_f32(3)
+    for d in (64, 128):
+        v = np.zeros((1, d), np.float32)
+        v[0, 0] = 1.0
+        n0, c0 = codec.v_encode(v, 3)
+        n1, c1 = codec.v_encode(v, 3, corrected_norm=True)
+        assert np.all(c0 == 5) and np.array_equal(c0, c1)
+        assert n0[0] == 1.0 and abs(float(n1[0]) * float(cent[5]) - 1.0) <= 2.0 ** -22  # n' = 1 / c_5 (2 ulp)
+        plain = codec.v_decode(n0, c0, 3)[0]
+        corr = codec.v_decode(n1, c1, 3)[0]
+        assert abs(plain[0] - cent[5]) < 1e-7 and np.max(np.abs(plain[1:])) < 1e-7
+        assert abs(corr[0] - 1.0) < 2e-7 and np.max(np.abs(corr[1:])) < 1e-7
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_corrected_norm_keeps_the_input_norm(bits, d):
+    """||v_hat|| = (n'/d) ||H c_hat|| = n' ||c_hat|| / sqrt(d) = ||v|| up to fp32 rounding; the codes
+    are the plain codec's; zero vectors keep norm 0."""
+    rng = np.random.default_rng(bits * d)
+    v = (rng.standard_normal((200, d)) * rng.lognormal(0, 1, (200, 1))).astype(np.float32)
+    v[3] = 0.0
+    n0, c0 = codec.v_encode(v, bits)
+    n1, c1 = codec.v_encode(v, bits, corrected_norm=True)
+    assert np.array_equal(c0, c1) and n1[3] == 0.0
+    vn = np.linalg.norm(v.astype(np.float64), axis=-1)
+    got = np.linalg.norm(codec.v_decode(n1, c1, bits), axis=-1)
+    ok = vn > 0
+    assert np.all(np.abs(got[ok] - vn[ok]) <= 4e-7 * vn[ok])
+    # the plain norm's decode is shorter by ||c_hat|| / sqrt(d), which is below 1 on average
+    plain = np.linalg.norm(codec.v_decode(n0, c0, bits), axis=-1)
+    assert np.mean(plain[ok] / vn[ok]) < 1.0

@@ -137,3 +137,38 @@ def test_shard_decodes_like_the_whole_pool_and_tiles_it():
         assert np.array_equal(s.ks, img.ks)
     with pytest.raises(ValueError):
         img.shard(3, 2)
+
+
+@pytest.mark.parametrize("k_scale", [pool_image.K_TOKEN, pool_image.K_CHANNEL])
+def test_variant_layouts_and_decoding(k_scale):
+    """Per-token scales take [L][Hkv][tc] floats, per-channel ones [L][Hkv][d] (and a per-channel
+    amax scratch); decoding uses each token's or channel's scale; a later append keeps the
+    first block's channel scales and every earlier byte."""
+    L, H, d, cap = 2, 3, 64, 70
+    lay = pool_image.layout(L, H, d, cap, [3, 2], k_scale)
+    base = pool_image.layout(L, H, d, cap, [3, 2])
+    ks_bytes = L * H * lay.tc * 4 if k_scale == pool_image.K_TOKEN else L * H * d * 4
+    assert lay.vmax - lay.ks >= ks_bytes and lay.vmax - lay.ks < ks_bytes + 256
+    assert lay.total >= base.total
+    rng = np.random.default_rng(5)
+    img = pool_image.PoolImage(L, H, d, cap, [3, 2], k_scale=k_scale)
+    k1 = rng.standard_normal((L, H, 40, d)).astype(np.float32)
+    v1 = rng.standard_normal((L, H, 40, d)).astype(np.float32)
+    img.append(0, k1, v1)
+    before = img.image().copy()
+    k2 = 3.0 * rng.standard_normal((L, H, 30, d)).astype(np.float32)
+    img.append(0, k2, rng.standard_normal((L, H, 30, d)).astype(np.float32))
+    after = img.image()
+    assert np.array_equal(after[lay.kq:lay.kq + L * H * lay.tc * d].reshape(L, H, lay.tc, d)[:, :, :40],
+                          before[lay.kq:lay.kq + L * H * lay.tc * d].reshape(L, H, lay.tc, d)[:, :, :40])
+    khat, _ = img.decoded_layer(1, 2)
+    if k_scale == pool_image.K_TOKEN:
+        s, q = codec.k_quantize_per_token(k2[1, 2])
+        assert np.array_equal(khat[40:], s[:, None].astype(np.float64) * q)
+    else:
+        s = codec.k_channel_scales(k1[1, 2])
+        assert np.array_equal(img.ks[1, 2], s)
+        assert np.array_equal(khat[40:], s[None, :].astype(np.float64) * codec.k_quantize_per_channel(k2[1, 2], s))
+        assert np.max(np.abs(img.kq[1, 2, 40:70])) == 127  # the larger later block clamps
+    sh = img.shard(1, 2)
+    assert np.array_equal(sh.decoded_layer(0, 1)[0], img.decoded_layer(0, 2)[0])
