@@ -62,7 +62,27 @@ typedef struct {
     int32_t capacity_tokens;         /* >= 1; rounded up to a multiple of 32 internally */
     uint8_t v_bits[PKV_MAX_LAYERS];  /* 2, 3 or 4 for layers 0 .. n_layers-1 */
     uint8_t v_signs[16];             /* rotation sign mask (see above); zero = plain FWHT */
+    uint8_t k_scale;                 /* K-scale granularity, PKV_KSCALE_* (0 = per tensor, the pages') */
+    uint8_t v_norm;                  /* stored V norm, PKV_VNORM_* (0 = plain ||v||) */
+    uint8_t reserved[2];             /* must be 0 */
 } pkv_pool_config;
+
+/* Codec variants, measured as ablations (PolyKV explainer, section 2.B names a
+ * per-tensor K scale and a per-vector V norm; the QKVShare blog, section 3.2,
+ * weighs per-tensor, per-token and per-channel granularity):
+ *  PKV_KSCALE_TENSOR   one scale per layer and append block (q8_0 over the block)
+ *  PKV_KSCALE_TOKEN    one scale per stored K vector (token, kv head)
+ *  PKV_KSCALE_CHANNEL  one scale per (layer, kv head, channel), taken from the
+ *                      first append; later appends use it and clamp at +-127
+ *  PKV_VNORM_PLAIN     Vn = ||v||
+ *  PKV_VNORM_CORRECTED Vn = fl(fl(||v|| * fl(sqrt(d))) / ||c_hat||), ||c_hat|| the
+ *                      fp32 norm of the chosen centroids (same halving tree), so
+ *                      the decoded vector keeps the input's norm; codes unchanged */
+#define PKV_KSCALE_TENSOR 0
+#define PKV_KSCALE_TOKEN 1
+#define PKV_KSCALE_CHANNEL 2
+#define PKV_VNORM_PLAIN 0
+#define PKV_VNORM_CORRECTED 1
 
 /*
  * Descriptor of one pool: a plain struct in caller-owned host memory (no
@@ -71,11 +91,12 @@ typedef struct {
  * region starting on a 256-byte boundary, with tc = capacity rounded up to 32:
  *
  *   Kq    int8 [L][Hkv][tc][d]            K codes (two's complement, -127..127)
- *   Vn    f32  [L][Hkv][tc]               V norms ||v|| (plain L2 norm)
+ *   Vn    f32  [L][Hkv][tc]               V norms (||v||, or the corrected norm)
  *   Ks    f32  [L][tc]                    K scale of the append block holding each token
+ *              ([L][Hkv][tc] per token, [L][Hkv][d] per channel)
  *   Vmax  f32  [L][Hkv]                   max V norm over the tokens stored so far
  *   Vc    u8   per layer l: [Hkv][tc/8][d * v_bits[l]]   packed V code groups
- *   amax  u32  [L]                        scratch used by pool_quantize_append
+ *   amax  u32  [L] ([L][Hkv][d] per channel)   scratch used by pool_quantize_append
  *
  * A V code group covers 8 consecutive tokens of one (layer, kv head): for
  * each dimension i = 0 .. d-1 in order, one little-endian field of
@@ -122,7 +143,8 @@ int pool_build(const pkv_pool_config* cfg, void* dev_buf, size_t dev_bytes, pkv_
  * Per layer, the K values of this call form one tensor with one scale:
  * s = amax / 127 (amax = max |k| over all heads, tokens and channels of that
  * layer in this call), codes = clamp(rint(k / s), -127, 127), or s = 0 and
- * codes 0 when amax = 0.  Each V vector x gets n = ||x|| (squares summed by a
+ * codes 0 when amax = 0 (PKV_KSCALE_TOKEN: the same rule per K vector;
+ * PKV_KSCALE_CHANNEL: per channel over the first append's tokens).  Each V vector x gets n = ||x|| (squares summed by a
  * halving tree, correctly rounded sqrt), z = H x (unnormalised Sylvester
  * Hadamard, butterflies with ascending half-width), y = z * (1/n), and
  * code_i = number of Lloyd-Max N(0, 1) thresholds strictly below y_i; n = 0
@@ -271,8 +293,9 @@ int pool_import(const pkv_pool_header* hdr, void* dev_buf, size_t dev_bytes, pkv
  * A pool holding kv heads [head_begin, head_begin + head_count) of src, laid
  * out in dev_buf (256-byte aligned, not overlapping src's buffer, dev_bytes >=
  * pool_bytes of src's config with n_kv_heads = head_count): per layer the K
- * codes, V norms, V maxima and V codes of those heads and all K scales are
- * copied (device to device, enqueued on stream); *out gets src's token counts.
+ * codes, V norms, V maxima and V codes of those heads, and the K scales (all of
+ * them per tensor; those heads' per token or per channel) are copied (device to
+ * device, enqueued on stream); *out gets src's token counts.
  * Decoding the shard with query heads [head_begin * G, (head_begin +
  * head_count) * G) of each agent gives the outputs the whole pool gives for
  * those heads (each (layer, kv head) is decoded independently), which is how

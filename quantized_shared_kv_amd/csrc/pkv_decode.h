@@ -31,7 +31,16 @@ struct PoolEntry {
     int32_t agent_base;    // >= 0: the pool's launch agents agent0 + i are call agents
                            // agent_base + i (no table lookup needed); -1 otherwise
     uint32_t vsign[4];     // V rotation sign mask: output dimension i negated after the inverse FWHT
+    int32_t kmode;         // K-scale granularity (PKV_KSCALE_*): where the K scale of a token lives
 };
+
+// K scales of pool layer l, kv head g: per tensor [tc] (shared by the heads), per token [tc],
+// per channel [d]
+__host__ __device__ inline uint64_t ks_offset(const PoolEntry& p, int l, int g, int hkv, int d) {
+    if (p.kmode == PKV_KSCALE_TOKEN) return ((uint64_t)l * hkv + g) * p.tc;
+    if (p.kmode == PKV_KSCALE_CHANNEL) return ((uint64_t)l * hkv + g) * d;
+    return (uint64_t)l * p.tc;
+}
 
 struct DecodeLaunch {
     PoolEntry pools[kMaxPoolsPerLaunch];

@@ -117,6 +117,7 @@ struct PoolSrc {
     const float* ks;
     const uint8_t* vc;
     const float* cent;
+    const float* kch;  // per-channel K scales, or nullptr (per tensor / per token: ks)
     int bits;
     float sm_log2;
     __device__ void load_tile(ValuSmem<D>& sm, int t0, int t_end) const {
@@ -124,7 +125,8 @@ struct PoolSrc {
         for (int idx = tid; idx < kTile * D; idx += kThreads) {
             const int t = idx / D, i = idx % D;
             const int tok = t0 + t;
-            sm.k[t][i] = tok < t_end ? static_cast<float>(kq[(uint64_t)tok * D + i]) : 0.0f;
+            const float k = tok < t_end ? static_cast<float>(kq[(uint64_t)tok * D + i]) : 0.0f;
+            sm.k[t][i] = kch ? k * kch[i] : k;
         }
         const uint32_t mask = (1u << bits) - 1u;
         for (int idx = tid; idx < 4 * D; idx += kThreads) {
@@ -138,7 +140,7 @@ struct PoolSrc {
             const int tok = t0 + tid;
             const bool ok = tok < t_end;
             sm.valid[tid] = ok;
-            sm.f[tid] = ok ? ks[tok] * sm_log2 : 0.0f;
+            sm.f[tid] = ok ? (kch ? sm_log2 : ks[tok] * sm_log2) : 0.0f;
             sm.nn[tid] = ok ? vn[tok] : 0.0f;
         }
     }
@@ -245,7 +247,8 @@ __global__ void __launch_bounds__(kThreads) k_pool_valu(DecodeLaunch a, Centroid
     PoolSrc<D> src;
     src.kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
     src.vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
-    src.ks = reinterpret_cast<const float*>(P.base + P.off_ks) + (uint64_t)l * P.tc;
+    src.ks = reinterpret_cast<const float*>(P.base + P.off_ks) + ks_offset(P, l, g, a.hkv, D);
+    src.kch = P.kmode == PKV_KSCALE_CHANNEL ? src.ks : nullptr;
     src.vc = P.base + P.off_vc0 + (uint64_t)a.hkv * P.tc * (D / 8) * layer_bits_prefix(P, l) +
              (uint64_t)g * (P.tc / kGroupTokens) * D * bits;
     src.cent = cents.c[bits - 2];
@@ -770,7 +773,7 @@ __device__ void seg_wave(const DecodeLaunch& a, const PoolEntry& P, int k, int j
     const int agent = P.agent_base >= 0 ? P.agent_base + jpos : a.agent_id[P.agent0 + jpos];
     const int8_t* kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
     const float* vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
-    const float* ks = reinterpret_cast<const float*>(P.base + P.off_ks) + (uint64_t)l * P.tc;
+    const float* ks = reinterpret_cast<const float*>(P.base + P.off_ks) + ks_offset(P, l, g, a.hkv, D);
     const uint8_t* vc = P.base + P.off_vc0 + (uint64_t)a.hkv * P.tc * (D / 8) * layer_bits_prefix(P, l) +
                         (uint64_t)g * (P.tc / 8) * D * BITS;
     const int part = lane % LPT, tl = lane / LPT;
@@ -1143,6 +1146,13 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
     auto private_of = [&](int a) -> const pkv_pool* {
         return x->agent_private_pool ? x->agent_private_pool[a] : nullptr;
     };
+    // fp32 queries, and queries that carry a per-channel pool's K scales, take the matrix-core
+    // kernel's fp16 hi + lo operands: at most 48 rows per workgroup
+    bool split_q = x->q_dtype == PKV_F32;
+    for (int a = 0; a < x->n_agents; ++a) {
+        split_q = split_q || x->agent_pool[a]->cfg.k_scale == PKV_KSCALE_CHANNEL;
+        if (private_of(a)) split_q = split_q || private_of(a)->cfg.k_scale == PKV_KSCALE_CHANNEL;
+    }
 
     // group agents by pool (first appearance order)
     std::vector<const pkv_pool*> order;
@@ -1216,6 +1226,7 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.off_vmax = p->off_vmax;
             e.off_vc0 = p->off_vc[0];
             std::memcpy(e.vsign, p->cfg.v_signs, sizeof(e.vsign));
+            e.kmode = p->cfg.k_scale;
             for (int l = 0; l < p->cfg.n_layers; ++l) {
                 if (p->cfg.v_bits[l] >= 3) e.ge3[l >> 5] |= 1u << (l & 31);
                 if (p->cfg.v_bits[l] == 4) e.eq4[l >> 5] |= 1u << (l & 31);
@@ -1228,7 +1239,7 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             const int tiles = std::max(1, (e.T + kTile - 1) / kTile);
             // row blocks: the matrix-core kernel holds at most 64 rows per workgroup (48 with fp32
             // queries), balanced over the blocks; the vector kernel 32
-            const int block_max = use_mfma ? (x->q_dtype == PKV_F32 ? 48 : 64) : kValuRows;
+            const int block_max = use_mfma ? (split_q ? 48 : 64) : kValuRows;
             e.rblocks = (e.rows + block_max - 1) / block_max;
             e.rb_rows = use_mfma ? (e.rows + e.rblocks - 1) / e.rblocks : kValuRows;
             int splits = x->splits;
@@ -1280,7 +1291,8 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
                 while (j < c.agents.size() && private_of(c.agents[j]) == q) ++j;
                 if (q) {
                     const std::vector<int> grp(c.agents.begin() + i, c.agents.begin() + j);
-                    const bool seg = x->q_dtype == PKV_BF16 && (int)grp.size() * G <= 8;
+                    const bool seg = x->q_dtype == PKV_BF16 && (int)grp.size() * G <= 8 &&
+                                     q->cfg.k_scale != PKV_KSCALE_CHANNEL;
                     const int ent = add_pool(q, n_agents + (int)i, grp, seg);
                     for (size_t t = i; t < j; ++t) {
                         L.agent_pool2[n_agents + t] = (int16_t)ent;

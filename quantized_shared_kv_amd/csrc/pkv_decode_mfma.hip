@@ -398,7 +398,11 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 
     const int8_t* kq = reinterpret_cast<const int8_t*>(P.base + P.off_kq) + ((uint64_t)l * a.hkv + g) * P.tc * D;
     const float* vn = reinterpret_cast<const float*>(P.base + P.off_vn) + ((uint64_t)l * a.hkv + g) * P.tc;
-    const float* ks = reinterpret_cast<const float*>(P.base + P.off_ks) + (uint64_t)l * P.tc;
+    // per-token K factors of the scores (Ks * sigma * log2 e, from the ring); a per-channel pool has
+    // its scales folded into the queries instead, its ring slot reads the norms a second time
+    const bool kchan = P.kmode == PKV_KSCALE_CHANNEL;
+    const float* ks = kchan ? vn : reinterpret_cast<const float*>(P.base + P.off_ks) + ks_offset(P, l, g, a.hkv, D);
+    const float* kch = reinterpret_cast<const float*>(P.base + P.off_ks) + ks_offset(P, l, g, a.hkv, D);
     const uint8_t* vc = P.base + P.off_vc0 + (uint64_t)a.hkv * P.tc * (D / 8) * layer_bits_prefix(P, l) +
                         (uint64_t)g * (P.tc / kGroupTokens) * D * BITS;
     const float vmax = reinterpret_cast<const float*>(P.base + P.off_vmax)[(uint64_t)l * a.hkv + g];
@@ -461,6 +465,9 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // entry per lane; then the ring, so that waiting for the set-up loads does not
     // wait for the ring
     constexpr int QV = QSPLIT ? 2 : 1;
+    // hi + lo query operands (QSPLIT) for fp32 queries, and for bf16 queries that carry a
+    // per-channel pool's K scales
+    const bool q32 = a.q_dtype == PKV_F32;
     uint4 qraw[RT][KS][QV];
     bool rok[RT];
     // the rows' agents and heads first (a table lookup only when the pool's agents are not
@@ -488,12 +495,23 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         const uint64_t qo = (((uint64_t)q_agent[rt] * a.lc + lj) * a.hq + q_head[rt]) * D + lg * DL;
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            if constexpr (QSPLIT) {
+            if (QSPLIT && q32) {
                 const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qo + 8 * k);
                 qraw[rt][k][0] = src[0];
                 qraw[rt][k][QV - 1] = src[1];
             } else {
                 qraw[rt][k][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + 8 * k);
+            }
+        }
+    }
+    // a per-channel pool's scales of this lane's query dimensions (lg*DL + 8 k + i), folded into q
+    float4 chs[QSPLIT ? KS : 1][2];
+    if constexpr (QSPLIT) {
+        if (kchan) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                chs[k][0] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k);
+                chs[k][1] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k + 4);
             }
         }
     }
@@ -520,7 +538,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             uint32_t w[8];
-            if constexpr (QSPLIT) {
+            if (QSPLIT && q32) {
                 const uint4 r0 = qraw[rt][k][0], r1 = qraw[rt][k][QV - 1];
                 w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
                 w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
@@ -536,6 +554,12 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 xs[k][i] = rok[rt] ? __uint_as_float(w[i]) : 0.0f;
+                if constexpr (QSPLIT) {
+                    if (kchan) {  // q'_i = q_i * s_i (fp32), split into fp16 hi + lo below
+                        const float4 c = chs[k][i >> 2];
+                        xs[k][i] *= (i & 3) == 0 ? c.x : (i & 3) == 1 ? c.y : (i & 3) == 2 ? c.z : c.w;
+                    }
+                }
                 mx = fmaxf(mx, fabsf(xs[k][i]));
             }
         }
@@ -604,6 +628,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                               (BITS == 3 ? 0u : BITS == 2 ? 8u * (lane & 15) : 4u * (lane & (kLutCopies - 1)));
     const uint32_t ring_a = lds_addr(ring);
     const float fs = a.sm_log2;
+    const float fs_tok = kchan ? 0.0f : fs, fs_const = kchan ? fs : 0.0f;  // ff = Ks * fs_tok + fs_const
 
     // wait until at most `groups` steps' loads issued after the one needed are in
     // flight (each step is SL::NDMA load instructions, completed in order)
@@ -662,7 +687,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             nn[i] = __uint_as_float(w[i]);
-            ff[i] = __uint_as_float(w[8 + i]) * fs;  // Ks * sigma * log2 e: scores in log2 units
+            ff[i] = fmaf(__uint_as_float(w[8 + i]), fs_tok, fs_const);  // Ks * sigma * log2 e: log2 units
         }
     };
 
@@ -1050,14 +1075,18 @@ int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int
 int launch_pool_mfma(const DecodeLaunch& a, int total_wg, hipStream_t s) {
     // rows per workgroup: the largest row block of the launch's pools (the plan keeps blocks at
     // most 64 rows, 48 with fp32 queries, whose hi + lo operands take twice the registers)
+    // fp32 queries, and queries carrying a per-channel pool's K scales, take fp16 hi + lo operands
     int rows = 1;
+    bool split = a.q_dtype == PKV_F32;
     for (int p = 0; p < a.n_pools; ++p)
-        if (a.pools[p].seg_begin < 0) rows = rows > a.pools[p].rb_rows ? rows : a.pools[p].rb_rows;
-    if (rows > (a.q_dtype == PKV_F32 ? 48 : kMaxRows)) return PKV_EUNSUPPORTED;
+        if (a.pools[p].seg_begin < 0) {
+            rows = rows > a.pools[p].rb_rows ? rows : a.pools[p].rb_rows;
+            split = split || a.pools[p].kmode == PKV_KSCALE_CHANNEL;
+        }
+    if (rows > (split ? 48 : kMaxRows)) return PKV_EUNSUPPORTED;
     const int rt = (rows + 15) / 16;
     CentArg c;
     std::memcpy(c.c, codebook_tables().cent, sizeof(c.c));
-    const bool split = a.q_dtype == PKV_F32;
     if (a.d == 128) return split ? launch_d<128, true>(a, total_wg, s, c, rt) : launch_d<128, false>(a, total_wg, s, c, rt);
     return split ? launch_d<64, true>(a, total_wg, s, c, rt) : launch_d<64, false>(a, total_wg, s, c, rt);
 }

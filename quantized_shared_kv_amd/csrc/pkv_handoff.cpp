@@ -87,10 +87,14 @@ int pool_shard(const pkv_pool* src, int32_t head_begin, int32_t head_count, void
     auto copy = [&](uint64_t dst_off, uint64_t src_off, uint64_t n) {
         return hipMemcpyAsync(db + dst_off, sb + src_off, n, hipMemcpyDeviceToDevice, s) == hipSuccess;
     };
-    bool ok = copy(p.off_ks, src->off_ks, L * tc * 4);  // K scales: shared by every head
+    // K scales: per tensor one per token, shared by every head (copied whole); per token
+    // [L][H][tc] and per channel [L][H][d] (the range's heads, layer by layer)
+    const uint64_t kper = cfg.k_scale == PKV_KSCALE_TOKEN ? tc : cfg.k_scale == PKV_KSCALE_CHANNEL ? d : 0;
+    bool ok = kper ? true : copy(p.off_ks, src->off_ks, L * tc * 4);
     for (uint64_t l = 0; ok && l < L; ++l) {
         const uint64_t bits = cfg.v_bits[l];
-        ok = copy(p.off_kq + l * hc * tc * d, src->off_kq + (l * H + h0) * tc * d, hc * tc * d) &&
+        ok = (!kper || copy(p.off_ks + l * hc * kper * 4, src->off_ks + (l * H + h0) * kper * 4, hc * kper * 4)) &&
+             copy(p.off_kq + l * hc * tc * d, src->off_kq + (l * H + h0) * tc * d, hc * tc * d) &&
              copy(p.off_vn + l * hc * tc * 4, src->off_vn + (l * H + h0) * tc * 4, hc * tc * 4) &&
              copy(p.off_vmax + l * hc * 4, src->off_vmax + (l * H + h0) * 4, hc * 4) &&
              copy(p.off_vc[l], src->off_vc[l] + h0 * (tc / 8) * d * bits, hc * (tc / 8) * d * bits);

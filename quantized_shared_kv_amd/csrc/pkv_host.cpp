@@ -87,9 +87,11 @@ bool config_valid(const pkv_pool_config* cfg, int* err) {
     if (cfg->head_dim != 64 && cfg->head_dim != 128) return false;
     for (int l = 0; l < cfg->n_layers; ++l)
         if (cfg->v_bits[l] < 2 || cfg->v_bits[l] > 4) return false;
+    if (cfg->k_scale > PKV_KSCALE_CHANNEL || cfg->v_norm > PKV_VNORM_CORRECTED) return false;
     *err = PKV_EINVAL;
     for (int i = cfg->head_dim / 8; i < 16; ++i)
         if (cfg->v_signs[i]) return false;  // sign bits past head_dim
+    if (cfg->reserved[0] || cfg->reserved[1]) return false;
     // keep every region offset inside 64-bit arithmetic with a wide margin
     const double est = (double)cfg->n_layers * cfg->n_kv_heads * ((double)cfg->capacity_tokens + 32) *
                        (cfg->head_dim * 1.5 + 8.0);
@@ -110,11 +112,14 @@ void fill_layout(const pkv_pool_config* cfg, pkv_pool* p) {
     p->off_kq = 0;
     p->off_vn = align_up(p->off_kq + L * H * tc * d);
     p->off_ks = align_up(p->off_vn + L * H * tc * 4);
-    p->off_vmax = align_up(p->off_ks + L * tc * 4);
+    const uint64_t ks_bytes = cfg->k_scale == PKV_KSCALE_TOKEN     ? L * H * tc * 4
+                              : cfg->k_scale == PKV_KSCALE_CHANNEL ? L * H * d * 4
+                                                                   : L * tc * 4;
+    p->off_vmax = align_up(p->off_ks + ks_bytes);
     p->off_vc[0] = align_up(p->off_vmax + L * H * 4);
     for (uint64_t l = 0; l < L; ++l) p->off_vc[l + 1] = p->off_vc[l] + H * tc * d * cfg->v_bits[l] / 8;
     p->off_amax = align_up(p->off_vc[L]);
-    p->bytes = align_up(p->off_amax + L * 4);
+    p->bytes = align_up(p->off_amax + (cfg->k_scale == PKV_KSCALE_CHANNEL ? L * H * d * 4 : L * 4));
 }
 
 }  // namespace
@@ -159,7 +164,7 @@ const char* pkv_strerror(int code) {
     }
 }
 
-int pkv_version(void) { return 105; }
+int pkv_version(void) { return 106; }
 
 size_t pkv_abi_sizeof(int32_t which) {
     switch (which) {

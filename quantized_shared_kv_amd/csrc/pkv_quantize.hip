@@ -10,6 +10,8 @@
 // Three launches per append, all on the caller's stream:
 //   1. k_reset      clear the per-layer amax scratch (and Vmax on a fresh layer)
 //   2. k_amax       max |k| per layer, reduced with an atomic max on fp32 bits
+//                   (k_amax_channel per (layer, kv head, channel) on a per-channel pool's
+//                   first append; none for per-token scales, found inside k_encode)
 //   3. k_encode     a wavefront encodes one 8-token code group of one (layer,
 //                   kv head) at a time: int8 K rows, then for the 8 tokens
 //                   together an in-register FWHT across the wave (head_dim 64:
@@ -18,7 +20,9 @@
 //                   are staged in LDS and stored as dwords.
 // Every floating-point step uses one IEEE rounding (no FMA contraction, correctly
 // rounded division and square root), so codes are reproducible bit for bit.
+#include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "pkv_internal.h"
 #include "pkv_lanes.h"
@@ -41,8 +45,17 @@ struct EncodeArgs {
     int32_t l0, nl;
     uint8_t bits[kMaxLayersArg];     // bits of each call layer
     float thr[3][15];
+    float cent[3][16];               // Lloyd-Max centroids (the corrected norm's ||c_hat||)
     uint32_t vsign[4];               // V rotation sign mask: bit i set = coordinate i negated
+    int32_t kmode;                   // PKV_KSCALE_*
+    int32_t vcorr;                   // corrected V norm
+    float sd;                        // fl(sqrt(head_dim))
 };
+
+// k_encode reads its EncodeArgs in place at the start of the kernel-argument segment, where the
+// first explicit argument of a kernel sits (HSA code-object ABI): a plain, standard-layout block.
+static_assert(std::is_standard_layout<EncodeArgs>::value && std::is_trivially_copyable<EncodeArgs>::value,
+              "EncodeArgs is read as raw kernel-argument memory");
 
 __device__ __forceinline__ float load_elem(const void* p, int dtype, uint64_t i) {
     if (dtype == PKV_BF16) {
@@ -56,7 +69,12 @@ __global__ void k_reset(EncodeArgs a) {
     const int j = blockIdx.x;
     if (j >= a.nl) return;
     const int l = a.l0 + j;
-    if (threadIdx.x == 0) reinterpret_cast<uint32_t*>(a.base + a.off_amax)[l] = 0u;
+    if (a.kmode == PKV_KSCALE_CHANNEL) {  // per (kv head, channel) maxima of the first append
+        uint32_t* am = reinterpret_cast<uint32_t*>(a.base + a.off_amax) + (uint64_t)l * a.hkv * a.d;
+        for (int i = threadIdx.x; i < a.hkv * a.d; i += blockDim.x) am[i] = 0u;
+    } else if (threadIdx.x == 0) {
+        reinterpret_cast<uint32_t*>(a.base + a.off_amax)[l] = 0u;
+    }
     if (a.t0 == 0) {
         float* vmax = reinterpret_cast<float*>(a.base + a.off_vmax);
         for (int g = threadIdx.x; g < a.hkv; g += blockDim.x) vmax[(uint64_t)l * a.hkv + g] = 0.0f;
@@ -130,6 +148,21 @@ __global__ void __launch_bounds__(256) k_amax(EncodeArgs a) {
         // non-negative floats order like their bit patterns
         atomicMax(reinterpret_cast<uint32_t*>(a.base + a.off_amax) + (a.l0 + j), __float_as_uint(r));
     }
+}
+
+// grid (kAmaxBlocks, hkv, nl), 256 threads: max |k| per (layer, kv head, channel) over the
+// append's tokens (a per-channel pool's first append).  Thread t reads channel t % d of every
+// (256 / d)-th token of its block's share, so a wavefront reads whole token rows.
+__global__ void __launch_bounds__(256) k_amax_channel(EncodeArgs a) {
+    const int j = blockIdx.z, g = blockIdx.y;
+    const int c = threadIdx.x % a.d, tl = threadIdx.x / a.d, tper = 256 / a.d;
+    const uint64_t row0 = ((uint64_t)j * a.hkv + g) * a.n;
+    float m = 0.0f;
+    for (int t = blockIdx.x * tper + tl; t < a.n; t += gridDim.x * tper)
+        m = fmaxf(m, fabsf(load_elem(a.k, a.dtype, (row0 + t) * a.d + c)));
+    // non-negative floats order like their bit patterns
+    uint32_t* am = reinterpret_cast<uint32_t*>(a.base + a.off_amax) + ((uint64_t)(a.l0 + j) * a.hkv + g) * a.d;
+    atomicMax(am + c, __float_as_uint(m));
 }
 
 constexpr int kEncWaves = 4;
@@ -237,7 +270,8 @@ __device__ __forceinline__ uint32_t lm_code(float y, const float* t) {
 // are independent and overlap.  Lane lam holds dimensions EPL*lam .. EPL*lam + EPL-1.
 template <int EPL, int BITS, bool BF16>
 __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g, int j, const EncRaw<EPL, BF16>& raw,
-                             uint8_t* stage, float& nmax) {
+                             uint8_t* stage, float& nmax, const float* cent, const float (&sch)[EPL],
+                             const float (&rch)[EPL], uint64_t off_vc) {
 #pragma clang fp contract(off)
     constexpr int D = 64 * EPL;
     const int lane = threadIdx.x & 63;
@@ -246,9 +280,6 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
 #pragma unroll
     for (int k = 0; k < (1 << BITS) - 1; ++k) thr[k] = a.thr[BITS - 2][k];
 
-    const float amax = __uint_as_float(reinterpret_cast<const uint32_t*>(a.base + a.off_amax)[l]);
-    const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
-    const float rs = s > 0.0f ? 1.0f / s : 0.0f;
 
     const int gt0 = grp * kGroupTokens;
     bool valid[kGroupTokens];
@@ -263,9 +294,40 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
             kx[i][e] = enc_elem<EPL, BF16>(raw.k[i], e);
             vx[i][e] = enc_elem<EPL, BF16>(raw.v[i], e);
         }
+    // ---- K scales: per tensor, one per layer and append (from k_amax); per token, each token's
+    // max |k| over the wavefront; per channel, this lane's channels' (sch)
+    float sk[kGroupTokens], rk[kGroupTokens];  // scale and its reciprocal per token
+    if (a.kmode == PKV_KSCALE_TENSOR) {
+        const float amax = __uint_as_float(reinterpret_cast<const uint32_t*>(a.base + a.off_amax)[l]);
+        const float s = amax > 0.0f ? amax / 127.0f : 0.0f;
+        const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i) {
+            sk[i] = s;
+            rk[i] = rs;
+        }
+    } else if (a.kmode == PKV_KSCALE_TOKEN) {
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i) {
+            float m = fabsf(kx[i][0]);
+            if (EPL == 2) m = fmaxf(m, fabsf(kx[i][EPL - 1]));
+            m = fmaxf(m, lane_xor<32>(m));
+            m = fmaxf(m, lane_xor<16>(m));
+            m = fmaxf(m, lane_xor<8>(m));
+            m = fmaxf(m, lane_xor<4>(m));
+            m = fmaxf(m, lane_xor<2>(m));
+            m = fmaxf(m, lane_xor<1>(m));
+            sk[i] = m > 0.0f ? m / 127.0f : 0.0f;
+            rk[i] = sk[i] > 0.0f ? 1.0f / sk[i] : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i) sk[i] = rk[i] = 0.0f;
+    }
     // ---- K rows: q = clamp(rint(k / s), -127, 127).  k * (1/s) is within 1.5e-5 of the
     // correctly rounded quotient (|k / s| <= 127), so it rounds the same way unless it lies
-    // within 3e-5 of a half-integer; only then is the quotient itself computed.
+    // within 3e-5 of a half-integer; only then is the quotient itself computed (past 127.5 the
+    // code clamps either way).
     int8_t* kq = reinterpret_cast<int8_t*>(a.base + a.off_kq) + ((uint64_t)l * a.hkv + g) * a.tc * D;
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) {
@@ -273,9 +335,11 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
+            const bool ch = a.kmode == PKV_KSCALE_CHANNEL;
+            const float s = ch ? sch[e] : sk[i];
             float q = 0.0f;
             if (s > 0.0f) {
-                const float t = kx[i][e] * rs;
+                const float t = kx[i][e] * (ch ? rch[e] : rk[i]);
                 const float fr = t - floorf(t);
                 q = rintf(t);
                 if (fabsf(fr - 0.5f) < 3.0e-5f) q = rintf(kx[i][e] / s);
@@ -322,7 +386,9 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
     // stage first when EPL == 2)
     {
         const int d0 = EPL * lane;
-        const uint32_t sb = (a.vsign[d0 >> 5] >> (d0 & 31)) & ((1u << EPL) - 1u);
+        const int wsel = d0 >> 5;  // a select over the four words, not an index into the argument block
+        const uint32_t word = wsel == 0 ? a.vsign[0] : wsel == 1 ? a.vsign[1] : wsel == 2 ? a.vsign[2] : a.vsign[3];
+        const uint32_t sb = (word >> (d0 & 31)) & ((1u << EPL) - 1u);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const uint32_t flip = ((sb >> e) & 1u) << 31;
@@ -346,16 +412,52 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
     butterfly<32>(vx, lane);
     // ---- codes of y = z * (1/n); 8 tokens per field
     uint32_t field[EPL];
+    uint32_t code[kGroupTokens][EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) field[e] = 0u;
 #pragma unroll
     for (int i = 0; i < kGroupTokens; ++i) {
-        if (!valid[i] || !(nrm[i] > 0.0f)) continue;
+        const bool coded = valid[i] && nrm[i] > 0.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) field[e] |= lm_code<BITS>(vx[i][e] * rcp[i], thr) << (BITS * i);
-        nmax = fmaxf(nmax, nrm[i]);
+        for (int e = 0; e < EPL; ++e) {
+            code[i][e] = coded ? lm_code<BITS>(vx[i][e] * rcp[i], thr) : 0u;
+            field[e] |= code[i][e] << (BITS * i);
+        }
     }
-    uint8_t* vc = a.base + a.off_vc[j] + ((uint64_t)g * (a.tc / kGroupTokens) + grp) * (uint64_t)(D * BITS);
+    // ---- the stored norm: ||v||, or the corrected n' = fl(fl(n * sqrt(d)) / ||c_hat||) with the
+    // centroids' squares summed by the same halving tree (lane i < 8 holds token i's)
+    float n_store = n_l;
+    if (a.vcorr) {
+        float cq[kGroupTokens][EPL];
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float c = cent[code[i][e]];
+                cq[i][e] = c * c;
+            }
+        tree_level<32>(cq);
+        tree_level<16>(cq);
+        tree_level<8>(cq);
+        tree_level<4>(cq);
+        tree_level<2>(cq);
+        tree_level<1>(cq);
+        float cs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kGroupTokens; ++i) {
+            float ss = cq[i][0];
+            if (EPL == 2) ss = cq[i][0] + cq[i][EPL - 1];
+            cs = lane == i ? ss : cs;
+        }
+        const float cn = sqrtf(cs);
+        n_store = n_l > 0.0f ? (n_l * a.sd) / cn : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kGroupTokens; ++i) {
+        const float ni = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(n_store), i));
+        if (valid[i] && nrm[i] > 0.0f) nmax = fmaxf(nmax, ni);
+    }
+    uint8_t* vc = a.base + off_vc + ((uint64_t)g * (a.tc / kGroupTokens) + grp) * (uint64_t)(D * BITS);
     if (gt0 < a.t0) {  // the append starts inside this group: keep the earlier tokens' bits
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -366,15 +468,21 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
             field[e] |= old & ((1u << (BITS * (a.t0 - gt0))) - 1u);
         }
     }
-    // ---- norms and scales of the valid tokens: lane i < 8 stores token i
+    // ---- norms and per-tensor / per-token scales of the valid tokens: lane i < 8 stores token i
     float* vn = reinterpret_cast<float*>(a.base + a.off_vn) + ((uint64_t)l * a.hkv + g) * a.tc;
-    float* ks = reinterpret_cast<float*>(a.base + a.off_ks) + (uint64_t)l * a.tc;
     bool mine_ok = false;
+    float s_mine = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGroupTokens; ++i) mine_ok = lane == i ? valid[i] : mine_ok;
+    for (int i = 0; i < kGroupTokens; ++i) {
+        mine_ok = lane == i ? valid[i] : mine_ok;
+        s_mine = lane == i ? sk[i] : s_mine;
+    }
     if (lane < kGroupTokens && mine_ok) {
-        vn[gt0 + lane] = n_l;
-        if (g == 0) ks[gt0 + lane] = s;
+        vn[gt0 + lane] = n_store;
+        if (a.kmode == PKV_KSCALE_TENSOR && g == 0)
+            reinterpret_cast<float*>(a.base + a.off_ks)[(uint64_t)l * a.tc + gt0 + lane] = s_mine;
+        else if (a.kmode == PKV_KSCALE_TOKEN)
+            reinterpret_cast<float*>(a.base + a.off_ks)[((uint64_t)l * a.hkv + g) * a.tc + gt0 + lane] = s_mine;
     }
     // ---- code fields: dimension dim -> bytes [dim*BITS, dim*BITS + BITS), staged in LDS
 #pragma unroll
@@ -392,11 +500,39 @@ __device__ __forceinline__ void encode_group(const EncodeArgs& a, int grp, int g
 // grid (ceil(groups / kGroupsPerWg), hkv, nl), 256 threads; each wavefront loads its next
 // group while it encodes the current one
 template <int EPL, int BITS, bool BF16>
-__device__ __forceinline__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp) {
+__device__ __forceinline__ void encode_wg(const EncodeArgs& a, int grp_first, int n_grp, uint64_t off_vc) {
     __shared__ __align__(16) uint8_t stage[kEncWaves][128 * 4];
     __shared__ float wmax[kEncWaves];
+    __shared__ float cent[16];
     const int wave = threadIdx.x >> 6;
     const int g = blockIdx.y, j = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) {  // compile-time indices: a thread-dependent index into the kernel
+                             // argument would copy the whole argument block to scratch
+#pragma unroll
+        for (int k = 0; k < 16; ++k) cent[k] = a.cent[BITS - 2][k];
+    }
+    // per-channel scales of this lane's channels: from the first append's maxima (and stored
+    // by the first workgroup of each (layer, kv head)), or as stored by it for later appends
+    float sch[EPL], rch[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sch[e] = rch[e] = 0.0f;
+    if (a.kmode == PKV_KSCALE_CHANNEL) {
+        const uint64_t cb = ((uint64_t)(a.l0 + j) * a.hkv + g) * a.d + EPL * lane;
+        float* ks = reinterpret_cast<float*>(a.base + a.off_ks);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            if (a.t0 == 0) {
+                const float amax = __uint_as_float(reinterpret_cast<const uint32_t*>(a.base + a.off_amax)[cb + e]);
+                sch[e] = amax > 0.0f ? amax / 127.0f : 0.0f;
+                if (blockIdx.x == 0 && wave == 0) ks[cb + e] = sch[e];
+            } else {
+                sch[e] = ks[cb + e];
+            }
+            rch[e] = sch[e] > 0.0f ? 1.0f / sch[e] : 0.0f;
+        }
+    }
+    __syncthreads();
     float nmax = 0.0f;
     const int gb = blockIdx.x * kGroupsPerWg;
     const int ge = min(n_grp, gb + kGroupsPerWg);
@@ -407,7 +543,7 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, int grp_first, in
             // the last group loads itself again rather than branching around the load
             EncRaw<EPL, BF16> nxt;
             enc_load<EPL, BF16>(a, grp_first + min(gi + kEncWaves, ge - 1), g, j, nxt);
-            encode_group<EPL, BITS, BF16>(a, grp_first + gi, g, j, cur, stage[wave], nmax);
+            encode_group<EPL, BITS, BF16>(a, grp_first + gi, g, j, cur, stage[wave], nmax, cent, sch, rch, off_vc);
             cur = nxt;
         }
     }
@@ -421,22 +557,28 @@ __device__ __forceinline__ void encode_wg(const EncodeArgs& a, int grp_first, in
 }
 
 template <bool BF16>
-__device__ __forceinline__ void encode_dispatch(const EncodeArgs& a, int grp_first, int n_grp) {
-    const int b = a.bits[blockIdx.z];
+__device__ __forceinline__ void encode_dispatch(const EncodeArgs& a, int grp_first, int n_grp, int b, uint64_t off_vc) {
     if (a.d == 128) {
-        if (b == 2) encode_wg<2, 2, BF16>(a, grp_first, n_grp);
-        else if (b == 3) encode_wg<2, 3, BF16>(a, grp_first, n_grp);
-        else encode_wg<2, 4, BF16>(a, grp_first, n_grp);
+        if (b == 2) encode_wg<2, 2, BF16>(a, grp_first, n_grp, off_vc);
+        else if (b == 3) encode_wg<2, 3, BF16>(a, grp_first, n_grp, off_vc);
+        else encode_wg<2, 4, BF16>(a, grp_first, n_grp, off_vc);
     } else {
-        if (b == 2) encode_wg<1, 2, BF16>(a, grp_first, n_grp);
-        else if (b == 3) encode_wg<1, 3, BF16>(a, grp_first, n_grp);
-        else encode_wg<1, 4, BF16>(a, grp_first, n_grp);
+        if (b == 2) encode_wg<1, 2, BF16>(a, grp_first, n_grp, off_vc);
+        else if (b == 3) encode_wg<1, 3, BF16>(a, grp_first, n_grp, off_vc);
+        else encode_wg<1, 4, BF16>(a, grp_first, n_grp, off_vc);
     }
 }
 
-__global__ void __launch_bounds__(256) k_encode(EncodeArgs a, int grp_first, int n_grp) {
-    if (a.dtype == PKV_BF16) encode_dispatch<true>(a, grp_first, n_grp);
-    else encode_dispatch<false>(a, grp_first, n_grp);
+// The argument block is read in place, through the kernel-argument segment (it is the first
+// argument, at offset 0): handing the by-value parameter to the large inlined body made the
+// compiler copy all of it to per-lane scratch first.
+__global__ void __launch_bounds__(256) k_encode(EncodeArgs args, int grp_first, int n_grp) {
+    (void)args;
+    const EncodeArgs& a = *static_cast<const EncodeArgs*>((const void*)__builtin_amdgcn_kernarg_segment_ptr());
+    const int b = a.bits[blockIdx.z];
+    const uint64_t off_vc = a.off_vc[blockIdx.z];
+    if (a.dtype == PKV_BF16) encode_dispatch<true>(a, grp_first, n_grp, b, off_vc);
+    else encode_dispatch<false>(a, grp_first, n_grp, b, off_vc);
 }
 
 }  // namespace
@@ -484,11 +626,18 @@ extern "C" int pool_quantize_append(pkv_pool* pool, int32_t layer_begin, int32_t
     a.l0 = layer_begin;
     a.nl = layer_count;
     std::memcpy(a.thr, codebook_tables().thr, sizeof(a.thr));
+    std::memcpy(a.cent, codebook_tables().cent, sizeof(a.cent));
     std::memcpy(a.vsign, c.v_signs, sizeof(a.vsign));
+    a.kmode = c.k_scale;
+    a.vcorr = c.v_norm == PKV_VNORM_CORRECTED;
+    a.sd = (float)std::sqrt((double)c.head_dim);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(k_reset, dim3(layer_count), dim3(64), 0, s, a);
-    hipLaunchKernelGGL(k_amax, dim3(kAmaxBlocks, layer_count), dim3(256), 0, s, a);
+    if (c.k_scale == PKV_KSCALE_TENSOR)
+        hipLaunchKernelGGL(k_amax, dim3(kAmaxBlocks, layer_count), dim3(256), 0, s, a);
+    else if (c.k_scale == PKV_KSCALE_CHANNEL && t0 == 0)
+        hipLaunchKernelGGL(k_amax_channel, dim3(kAmaxBlocks, c.n_kv_heads, layer_count), dim3(256), 0, s, a);
     const int grp_first = t0 / kGroupTokens;
     const int grp_last = (t0 + n_tokens - 1) / kGroupTokens;
     const int n_grp = grp_last - grp_first + 1;

@@ -14,7 +14,7 @@ from ctypes import POINTER, c_float, c_int32, c_size_t, c_uint8, c_uint64, c_voi
 
 MAX_LAYERS = 128
 PKV_F32, PKV_BF16 = 0, 1
-ABI_VERSION = 105  # pkv_version() of the library these ctypes mirrors describe
+ABI_VERSION = 106  # pkv_version() of the library these ctypes mirrors describe
 KERNEL_DEFAULT, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 ERRORS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_ECAPACITY", -4: "PKV_ENOSPACE",
           -5: "PKV_EHIP"}
@@ -28,9 +28,14 @@ class PolyKVError(RuntimeError):
         super().__init__(f"{where}: {ERRORS.get(code, code)} ({lib().pkv_strerror(code).decode()})")
 
 
+KSCALE_TENSOR, KSCALE_TOKEN, KSCALE_CHANNEL = 0, 1, 2
+VNORM_PLAIN, VNORM_CORRECTED = 0, 1
+
+
 class PoolConfig(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
-                ("capacity_tokens", c_int32), ("v_bits", c_uint8 * MAX_LAYERS), ("v_signs", c_uint8 * 16)]
+                ("capacity_tokens", c_int32), ("v_bits", c_uint8 * MAX_LAYERS), ("v_signs", c_uint8 * 16),
+                ("k_scale", c_uint8), ("v_norm", c_uint8), ("reserved", c_uint8 * 2)]
 
 
 class Pool(ctypes.Structure):
@@ -139,9 +144,11 @@ def _stream_handle(stream) -> int | None:
 
 
 def make_config(n_layers: int, n_kv_heads: int, head_dim: int, capacity_tokens: int, v_bits,
-                v_signs=None) -> PoolConfig:
-    """v_signs: optional head_dim values, negative (or True) where the V rotation negates a coordinate."""
+                v_signs=None, k_scale: int = KSCALE_TENSOR, v_norm: int = VNORM_PLAIN) -> PoolConfig:
+    """v_signs: optional head_dim values, negative (or True) where the V rotation negates a coordinate.
+    k_scale: KSCALE_TENSOR / KSCALE_TOKEN / KSCALE_CHANNEL; v_norm: VNORM_PLAIN / VNORM_CORRECTED."""
     cfg = PoolConfig(n_layers, n_kv_heads, head_dim, capacity_tokens)
+    cfg.k_scale, cfg.v_norm = k_scale, v_norm
     vb = list(v_bits) if hasattr(v_bits, "__len__") else [int(v_bits)] * n_layers
     for i, b in enumerate(vb):
         cfg.v_bits[i] = int(b)

@@ -25,8 +25,9 @@ def to_device(t) -> torch.Tensor:
 class DevicePool:
     """A pool in a torch-owned device buffer."""
 
-    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=None):
-        self._allocate(pk.make_config(n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=v_signs))
+    def __init__(self, n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=None, k_scale=0, v_norm=0):
+        self._allocate(pk.make_config(n_layers, n_kv_heads, head_dim, capacity, bits, v_signs=v_signs,
+                                      k_scale=k_scale, v_norm=v_norm))
 
     @classmethod
     def empty_for(cls, cfg) -> "DevicePool":
@@ -56,16 +57,17 @@ def stack_layers(tensors):
     return torch.stack([to_device(t) for t in tensors]).contiguous()
 
 
-def build_pair(w, pool_id, layers=None, capacity=None, chunks=None):
+def build_pair(w, pool_id, layers=None, capacity=None, chunks=None, k_scale=0, v_norm=0):
     """(DevicePool, oracle PoolImage) for one pool of workload w, appended in the same chunks.
 
     chunks: list of token counts appended one after the other (default: all at once).
+    k_scale, v_norm: the pool's codec variant (pkv K-scale granularity, corrected V norm).
     """
     L = w.n_layers if layers is None else layers
     bits = w.v_bits(pool_id)[:L]
     cap = capacity or w.pool_tokens
-    dp = DevicePool(L, w.n_kv_heads, w.head_dim, cap, bits)
-    ref = pool_image.PoolImage(L, w.n_kv_heads, w.head_dim, cap, bits)
+    dp = DevicePool(L, w.n_kv_heads, w.head_dim, cap, bits, k_scale=k_scale, v_norm=v_norm)
+    ref = pool_image.PoolImage(L, w.n_kv_heads, w.head_dim, cap, bits, k_scale=k_scale, corrected_norm=bool(v_norm))
     ks = [w.pool_k(pool_id, l) for l in range(L)]
     vs = [w.pool_v(pool_id, l) for l in range(L)]
     chunks = chunks or [w.pool_tokens]
@@ -102,8 +104,13 @@ def compare_image(dp: DevicePool, ref: pool_image.PoolImage) -> dict:
     out["kq"] = int(np.sum(kq[:, :, :T] != ref.kq[:, :, :T]))
     vn = buf[lay.vn:lay.vn + L * H * tc * 4].view(np.uint32).reshape(L, H, tc)
     out["vn"] = int(np.sum(vn[:, :, :T] != ref.vn[:, :, :T].view(np.uint32)))
-    ks = buf[lay.ks:lay.ks + L * tc * 4].view(np.uint32).reshape(L, tc)
-    out["ks"] = int(np.sum(ks[:, :T] != ref.ks[:, :T].view(np.uint32)))
+    ks = buf[lay.ks:lay.ks + ref.ks.nbytes].view(np.uint32).reshape(ref.ks.shape)
+    if lay.k_scale == pool_image.K_TENSOR:
+        out["ks"] = int(np.sum(ks[:, :T] != ref.ks[:, :T].view(np.uint32)))
+    elif lay.k_scale == pool_image.K_TOKEN:
+        out["ks"] = int(np.sum(ks[:, :, :T] != ref.ks[:, :, :T].view(np.uint32)))
+    else:
+        out["ks"] = int(np.sum(ks != ref.ks.view(np.uint32)))
     vmax = buf[lay.vmax:lay.vmax + L * H * 4].view(np.uint32).reshape(L, H)
     out["vmax"] = int(np.sum(vmax != ref.vmax.view(np.uint32)))
     ngrp = (T + 7) // 8

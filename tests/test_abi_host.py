@@ -322,3 +322,26 @@ def test_stream_read_validation_is_host_side():
     assert f(ctypes.c_void_p((1 << 20) + 8), 16, sink, None) == -1   # src not 16-byte aligned
     assert f(ctypes.c_void_p(1 << 20), 24, sink, None) == -1          # bytes not a multiple of 16
     assert lib.pkv_stream_read_sink_words() > 0
+
+
+@pytest.mark.parametrize("k_scale", [0, 1, 2])
+@pytest.mark.parametrize("v_norm", [0, 1])
+def test_variant_layouts_match_oracle(k_scale, v_norm):
+    for L, H, d, cap, bits in ((3, 2, 128, 33, [2, 4, 3]), (32, 8, 128, 4096, [3] * 32), (5, 3, 64, 1, [4] * 5)):
+        cfg = pk.make_config(L, H, d, cap, bits, k_scale=k_scale, v_norm=v_norm)
+        ref = pool_image.layout(L, H, d, cap, bits, k_scale)
+        assert pk.pool_bytes(cfg) == ref.total
+        pool = pk.pool_build(cfg, 256 * 1024, ref.total)
+        assert (pool.off_ks, pool.off_vmax, pool.off_amax) == (ref.ks, ref.vmax, ref.amax)
+        assert list(pool.off_vc[:L + 1]) == ref.vc
+
+
+def test_variant_config_validation():
+    cfg = pk.make_config(2, 2, 64, 40, [3, 3], k_scale=3)
+    assert pk.pool_bytes(cfg) == 0 and pk.lib().pool_build(ctypes.byref(cfg), ctypes.c_void_p(4096), 1 << 20,
+                                                          ctypes.byref(pk.Pool())) == -2
+    cfg = pk.make_config(2, 2, 64, 40, [3, 3], v_norm=2)
+    assert pk.pool_bytes(cfg) == 0
+    cfg = pk.make_config(2, 2, 64, 40, [3, 3])
+    cfg.reserved[1] = 1
+    assert pk.pool_bytes(cfg) == 0
