@@ -262,7 +262,11 @@ def agent_decode_attention(pools, q, out, layer_begin=0, sfx_k=None, sfx_v=None,
         _check(lib().agent_decode_attention(ctypes.byref(a), None, ctypes.byref(size), None), "agent_decode_attention")
         return int(size.value)
     size.value = workspace.numel() * workspace.element_size()
-    _check(lib().agent_decode_attention(ctypes.byref(a), c_void_p(workspace.data_ptr()), ctypes.byref(size),
+    ws_ptr = workspace.data_ptr()
+    if not ws_ptr:
+        # the C call reads a NULL workspace as a size query and would enqueue nothing
+        raise ValueError("workspace has no device address (a zero-size tensor); allocate at least 256 bytes")
+    _check(lib().agent_decode_attention(ctypes.byref(a), c_void_p(ws_ptr), ctypes.byref(size),
                                         c_void_p(_stream_handle(stream))), "agent_decode_attention")
     del keep
     return int(size.value)

@@ -296,6 +296,31 @@ def test_binding_rejects_bad_tensors_before_any_launch():
                                       sfx_len=[0, 5, 16], workspace=_FakeWs(1 << 28, 1 << 20)), what
 
 
+def test_binding_rejects_a_workspace_without_address():
+    """A zero-size workspace tensor has address 0, which the C call would take as a size query
+    and so enqueue nothing; the binding raises instead."""
+    pool = _fake_pool(L=2, H=2, d=64, cap=100)
+    pool.n_tokens[0] = pool.n_tokens[1] = 70
+    A, lc, hq, d = 3, 2, 4, 64
+    q = _FakeT((A, lc, hq, d), 1 << 24)
+    out = _FakeT((A, lc, hq, d), 1 << 25, "f32")
+    with pytest.raises(ValueError, match="no device address"):
+        pk.agent_decode_attention([pool] * A, q, out, workspace=_NullWs())
+
+
+class _NullWs:
+    """A zero-size device tensor stand-in: address 0."""
+
+    def data_ptr(self):
+        return 0
+
+    def numel(self):
+        return 0
+
+    def element_size(self):
+        return 1
+
+
 class _FakeWs:
     """A workspace stand-in that must never reach the library in the tests that use it."""
 

@@ -5,11 +5,14 @@ At full size the oracle cannot check every output, so each case:
 * builds every pool of the workload on the device at its full size and bit widths;
   the sampled (pool, layer) slices come from the seeded workload generators, the
   rest (only where generating them on the host would take minutes) from a seeded
-  device-side draw of the same shape;
+  device-side draw of the same shape and value recipe (N(0, 1) times LogNormal(0, 0.5)
+  channel scales for the LogNormal workloads);
 * compares the pool image of every sampled layer byte for byte with the oracle's
   encoding of that layer (the codec is per layer, so one layer is checked alone);
-* runs one all-layer decode call for all agents with the default kernel and plan
-  (what ``bench.py`` times) and compares sampled output rows with the oracle's fp64
+* runs all-layer decode calls for all agents with the default kernel and plan
+  (what ``bench.py`` times) at the workload's decode steps -- every step of the
+  64-step SmolLM2 job (its suffix grows 1 .. 64), steps {0, middle, last} of the
+  others -- and compares sampled output rows of each with the oracle's fp64
   attention over its own decoded pool plus the agent's bf16 suffix (1e-3);
 * checks properties of every output row: finite, and within the range of the
   value vectors it averages (attention is a convex combination).
@@ -38,12 +41,12 @@ def _need_gpu():
 
 TOL = 1e-3
 
-# workload, decode step (suffix length is min(step + 1, S) for growing suffixes), every layer from the host
+# workload, decode steps (suffix length is min(step + 1, S) for growing suffixes), every layer from the host
 FULL_CASES = {
-    "smollm2_L24_H32_d64_T1851_A3": (wl.SMOLLM2, 63, True),
-    "llama3_8b_L32_d128_T4096_A15": (wl.LLAMA3_8B, 127, True),
-    "llama3_8b_long_T7194_S256_A15": (wl.LLAMA3_8B_LONG, 0, False),
-    "qwen3_32b_comix_L64_T8064_A8_pools8": (wl.QWEN3_32B_MIXED, 0, False),
+    "smollm2_L24_H32_d64_T1851_A3": (wl.SMOLLM2, list(range(64)), True),
+    "llama3_8b_L32_d128_T4096_A15": (wl.LLAMA3_8B, [0, 63, 127], True),
+    "llama3_8b_long_T7194_S256_A15": (wl.LLAMA3_8B_LONG, [0, 15, 31], False),
+    "qwen3_32b_comix_L64_T8064_A8_pools8": (wl.QWEN3_32B_MIXED, [0, 7, 15], False),
 }
 
 
@@ -69,18 +72,24 @@ def _layer_bytes(buf: np.ndarray, lay, l: int, T: int):
 
 @pytest.mark.parametrize("case", sorted(FULL_CASES))
 def test_full_size_pool_and_decode(case):
-    w, step, host_all = FULL_CASES[case]
+    w, steps, host_all = FULL_CASES[case]
     print(f"[fullsize] {case}", flush=True)
     A, L, Hkv, Hq, d, T, S = w.n_agents, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens, w.sfx_tokens
     G = Hq // Hkv
     n_pools = w.n_pools
     pool_of = [a % n_pools for a in range(A)]
-    s_len = _sfx_len(w, step)
     s_agents = sorted({0, A // 2, A - 1})
     s_layers = sorted({0, L // 2, L - 1})
     s_pools = sorted({pool_of[a] for a in s_agents})
     gen = torch.Generator(device=DEV)
     gen.manual_seed(1234)
+
+    def device_draw(shape):
+        """A seeded device draw with the workload's value recipe (channel scales on the last axis)."""
+        x = torch.randn(shape, generator=gen, device=DEV)
+        if w.dist == "lognormal_channels":
+            x = x * torch.exp(0.5 * torch.randn((Hkv,) + (1,) * (len(shape) - 2) + (d,), generator=gen, device=DEV))
+        return x.to(torch.bfloat16)
 
     def host_slice(kind, idx, l):
         return host_all or (l in s_layers and idx in (s_pools if kind == "pool" else s_agents))
@@ -102,8 +111,8 @@ def test_full_size_pool_and_decode(case):
                     ref.append(0, kt.f32[None], vt.f32[None])
                     refs[(p, l)] = ref
             else:
-                kd = torch.randn((1, Hkv, T, d), generator=gen, device=DEV).to(torch.bfloat16)
-                vd = torch.randn((1, Hkv, T, d), generator=gen, device=DEV).to(torch.bfloat16)
+                kd = device_draw((Hkv, T, d))[None].contiguous()
+                vd = device_draw((Hkv, T, d))[None].contiguous()
             pk.pool_quantize_append(pool, l, kd, vd)
         pools.append(pool)
         bufs.append(buf)
@@ -132,14 +141,28 @@ def test_full_size_pool_and_decode(case):
                 if a in s_agents and l in s_layers:
                     sfx_host[(a, l)] = (kt.f32, vt.f32)
             else:
-                sfx_k[a, l].copy_(torch.randn((Hkv, S, d), generator=gen, device=DEV).to(torch.bfloat16))
-                sfx_v[a, l].copy_(torch.randn((Hkv, S, d), generator=gen, device=DEV).to(torch.bfloat16))
+                sfx_k[a, l].copy_(device_draw((Hkv, S, d)))
+                sfx_v[a, l].copy_(device_draw((Hkv, S, d)))
+    agent_pools = [pools[pool_of[a]] for a in range(A)]
+    decoded = {}
+    worst = 0.0
+    for step in steps:
+        worst = max(worst, _check_step(case, w, step, agent_pools, bufs, refs, sfx_k, sfx_v, sfx_host, pool_of,
+                                       s_agents, s_layers, decoded))
+    print(f"[fullsize] {case}: {len(steps)} decode steps, worst sampled error {worst:.2e}", flush=True)
+
+
+def _check_step(case, w, step, agent_pools, bufs, refs, sfx_k, sfx_v, sfx_host, pool_of, s_agents, s_layers,
+                decoded):
+    """One all-layer decode call at `step` (default kernel and plan) and its checks; returns the
+    worst sampled error."""
+    A, L, Hkv, Hq, d, T = w.n_agents, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens
+    G = Hq // Hkv
+    n_pools = w.n_pools
+    s_len = _sfx_len(w, step)
     qs = [w.queries(step, a) for a in range(A)]
     q = torch.stack([to_device(t) for t in qs]).contiguous()
-
-    # ---- one all-layer call, default kernel and plan
     out = torch.full((A, L, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
-    agent_pools = [pools[pool_of[a]] for a in range(A)]
     lens = [s_len] * A
     ws_bytes = pk.agent_decode_attention(agent_pools, q, out, 0, sfx_k, sfx_v, lens)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
@@ -150,7 +173,7 @@ def test_full_size_pool_and_decode(case):
     # properties of every row: finite, inside the range of what it averages (a decoded pool value
     # is at most its vector's norm times the largest centroid, below 3 for 2-4 bits; suffix values
     # by their own maximum)
-    assert np.all(np.isfinite(o)), case
+    assert np.all(np.isfinite(o)), (case, step)
     vmax_all = np.zeros((A, L))
     for p in range(n_pools):
         lay = pool_image.layout(L, Hkv, d, T, w.v_bits(p))
@@ -160,7 +183,7 @@ def test_full_size_pool_and_decode(case):
                 vmax_all[a] = 3.0 * vm.max(axis=1)
     smax = sfx_v[:, :, :, :s_len].abs().amax(dim=(2, 3, 4)).float().cpu().numpy()
     bound = np.maximum(vmax_all, smax)[:, :, None, None] * 1.001
-    assert np.all(np.abs(o) <= bound), case
+    assert np.all(np.abs(o) <= bound), (case, step)
 
     # ---- sampled rows against the oracle
     worst = 0.0
@@ -171,10 +194,12 @@ def test_full_size_pool_and_decode(case):
             ksf, vsf = sfx_host[(a, l)]
             for h in heads:
                 g = h // G
-                khat, vhat = ref.decoded_layer(0, g)
+                if (pool_of[a], l, g) not in decoded:
+                    decoded[(pool_of[a], l, g)] = ref.decoded_layer(0, g)
+                khat, vhat = decoded[(pool_of[a], l, g)]
                 r = attention.attend_pool_and_suffix(qs[a].f32[l, h:h + 1], khat, vhat,
                                                      ksf[g, :s_len], vsf[g, :s_len])[0]
                 err = attention.max_rel_error(o[a, l, h][None], r[None])
                 worst = max(worst, err)
-                assert err <= TOL, (case, a, l, h, err)
-    print(f"[fullsize] {case}: worst sampled error {worst:.2e}", flush=True)
+                assert err <= TOL, (case, step, a, l, h, err)
+    return worst
