@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--comix", action="store_true",
                     help="instead of the decode job: time the CoMixKV controller (sensitivity kernel + allocation) "
                          "on the Qwen3-32B shape and measure the attention error of its bits against uniform 3 bits")
+    ap.add_argument("--codec-ablation", action="store_true",
+                    help="instead of the decode job: reconstruction error, attention error, bytes per token and "
+                         "pool-kernel time of the codec variants (K per tensor / token / channel, corrected V norm)")
     ap.add_argument("--rotation-ablation", action="store_true",
                     help="instead of the decode job: attention error and pool-kernel time of the plain FWHT "
                          "against a randomized (signed) rotation, on Gaussian and on Hadamard-aligned V")
@@ -164,6 +167,9 @@ def main():
     if args.rotation_ablation:
         rotation_ablation()
         return
+    if args.codec_ablation:
+        codec_ablation()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode.",
               file=sys.stderr)
@@ -232,7 +238,7 @@ def main():
             pk.pool_quantize_append(prv_pools[a], 0, *prv_kv[a])
     ws_bytes = pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A, kernel=kernel,
                                          private_pools=prv_pools)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in {time.time() - t0:.1f}s; pool {nbytes / 1e6:.1f} MB, workspace "
         f"{ws_bytes / 1e6:.1f} MB")
@@ -544,8 +550,8 @@ def qwen_bench(args):
     pools = [pk.pool_build(c, b.data_ptr(), b.numel()) for c, b in zip(cfgs, bufs)]
     for p in range(A):
         pk.pool_quantize_append(pools[p], 0, *kv[p])
-    ws = torch.empty(pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(pk.agent_decode_attention(pools, q_all[0], out, 0, sfx_k, sfx_v, [S] * A), 256),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in {time.time() - t0:.1f}s; pools {sum(b.numel() for b in bufs) / 1e9:.2f} GB")
     EV_EVERY = 4
@@ -686,6 +692,117 @@ def rotation_ablation():
                       "results": res}), flush=True)
 
 
+def codec_ablation():
+    """Codec variants on the Llama-3-8B-shaped workload (32 layers, 8 kv heads, d 128, 4096 pool
+    tokens, 3 bits, K and V with LogNormal(0, 0.5) channel scales, 15 agents x 4 query steps).
+
+    Per variant: K and V relative reconstruction error (sum of squared errors over the sum of
+    squares, the pool's bytes dequantised here with torch from the documented layout and the
+    library's centroid table), attention error per output row (relative L2 against fp32 torch
+    attention over the same bf16 K/V), bytes per token and kv head, and the pool kernel's time
+    (events; warm, and cold after a reduction over 1 GiB).
+    """
+    import torch
+
+    import workloads as wl
+    from quantized_shared_kv_amd import polykv as pk
+
+    pk.lib()
+    w = wl.LLAMA3_8B
+    dev = "cuda:0"
+    L, Hkv, Hq, d, T, A, G = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.pool_tokens, w.n_agents, w.group
+    R = 4
+
+    def dev_bf16(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k = torch.stack([dev_bf16(w.pool_k(0, l).raw) for l in range(L)])
+    v = torch.stack([dev_bf16(w.pool_v(0, l).raw) for l in range(L)])
+    qs = [torch.stack([dev_bf16(w.queries(s, a).raw) for a in range(A)]).contiguous() for s in range(R)]
+    kf, vf = k.float(), v.float()
+    h = torch.ones((1, 1), device=dev)
+    while h.shape[0] < d:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    cent = torch.tensor(pk.lloyd_max_table(3)[0], dtype=torch.float64, device=dev)
+    sigma = 1.0 / np.sqrt(d)
+    # exact attention per (step, layer): rows (agent, q head) grouped by kv head
+    refs = []
+    for s in range(R):
+        qf = qs[s].float()  # [A][L][Hq][d]
+        ref = torch.empty_like(qf)
+        for l in range(L):
+            qg = qf[:, l].reshape(A, Hkv, G, d).permute(1, 0, 2, 3).reshape(Hkv, A * G, d)
+            sc = torch.matmul(qg, kf[l].transpose(1, 2).contiguous()) * sigma
+            o = torch.matmul(torch.softmax(sc, dim=-1), vf[l])
+            ref[:, l] = o.reshape(Hkv, A, G, d).permute(1, 0, 2, 3).reshape(A, Hq, d)
+        refs.append(ref)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    variants = {"k_tensor (pages)": (pk.KSCALE_TENSOR, pk.VNORM_PLAIN), "k_token": (pk.KSCALE_TOKEN, pk.VNORM_PLAIN),
+                "k_channel": (pk.KSCALE_CHANNEL, pk.VNORM_PLAIN),
+                "v_corrected_norm": (pk.KSCALE_TENSOR, pk.VNORM_CORRECTED)}
+    res = {}
+    for name, (ks_mode, vn_mode) in variants.items():
+        cfg = pk.make_config(L, Hkv, d, T, [3] * L, k_scale=ks_mode, v_norm=vn_mode)
+        nb = pk.pool_bytes(cfg)
+        buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+        pool = pk.pool_build(cfg, buf.data_ptr(), nb)
+        pk.pool_quantize_append(pool, 0, k, v)
+        torch.cuda.synchronize()
+        tc = pool.tc
+        # dequantise from the image: K_hat = Ks * Kq, V_hat = (Vn / d) H c[code]
+        kq = buf[pool.off_kq:pool.off_kq + L * Hkv * tc * d].view(torch.int8).view(L, Hkv, tc, d)[:, :, :T].double()
+        ksb = buf[pool.off_ks:pool.off_vmax]
+        if ks_mode == pk.KSCALE_TENSOR:
+            sc = ksb[:L * tc * 4].view(torch.float32).view(L, 1, tc, 1)[:, :, :T]
+        elif ks_mode == pk.KSCALE_TOKEN:
+            sc = ksb[:L * Hkv * tc * 4].view(torch.float32).view(L, Hkv, tc, 1)[:, :, :T]
+        else:
+            sc = ksb[:L * Hkv * d * 4].view(torch.float32).view(L, Hkv, 1, d)
+        khat = kq * sc.double()
+        vn = buf[pool.off_vn:pool.off_vn + L * Hkv * tc * 4].view(torch.float32).view(L, Hkv, tc)[:, :, :T].double()
+        vc = buf[pool.off_vc[0]:pool.off_vc[L]].view(L, Hkv, tc // 8, d, 3).long()
+        field = vc[..., 0] | (vc[..., 1] << 8) | (vc[..., 2] << 16)  # [L][Hkv][groups][d]
+        codes = torch.stack([(field >> (3 * i)) & 7 for i in range(8)], dim=3).reshape(L, Hkv, tc, d)[:, :, :T]
+        vhat = (vn[..., None] / d) * torch.matmul(cent[codes], h.double())
+        k_err = float(((khat - kf.double()) ** 2).sum() / (kf.double() ** 2).sum())
+        v_err = float(((vhat - vf.double()) ** 2).sum() / (vf.double() ** 2).sum())
+        del kq, khat, vn, vc, field, codes, vhat
+        out = torch.empty((A, L, Hq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(pk.agent_decode_attention([pool] * A, qs[0], out, 0), 256), dtype=torch.uint8,
+                         device=dev)
+        errs = []
+        for s in range(R):
+            pk.agent_decode_attention([pool] * A, qs[s], out, 0, workspace=ws)
+            torch.cuda.synchronize()
+            errs.append(((out.double() - refs[s].double()).norm(dim=-1) / refs[s].double().norm(dim=-1)).flatten())
+        e = torch.cat(errs)
+        warm, cold = [], []
+        for i in range(12):
+            pk.agent_decode_attention([pool] * A, qs[i % R], out, 0, workspace=ws, pool_events=(e0, e1))
+            torch.cuda.synchronize()
+            warm.append(1e3 * e0.elapsed_time(e1))
+        for i in range(8):
+            flush.sum()
+            pk.agent_decode_attention([pool] * A, qs[i % R], out, 0, workspace=ws, pool_events=(e0, e1))
+            torch.cuda.synchronize()
+            cold.append(1e3 * e0.elapsed_time(e1))
+        res[name] = {"k_rel_sq_error": k_err, "v_rel_sq_error": v_err,
+                     "attention_rel_error_mean": float(e.mean()), "attention_rel_error_max": float(e.max()),
+                     "pool_bytes": nb, "bytes_per_token_per_kv_head": nb / (L * Hkv * T),
+                     "pool_kernel_us_warm": float(np.median(warm[2:])), "pool_kernel_us_cold": float(np.mean(cold))}
+        log(f"[codec] {name}: {json.dumps(res[name])}")
+        del buf
+    print(json.dumps({"metric": "codec variants: reconstruction and attention error, bytes, pool-kernel time",
+                      "value": res["k_tensor (pages)"]["attention_rel_error_mean"], "unit": "relative L2 error",
+                      "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": w.name, "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": d,
+                                 "pool_tokens": T, "agents": A, "v_bits": 3, "query_steps": R},
+                      "results": res}), flush=True)
+
+
 def comix_bench():
     """CoMixKV controller on the Qwen3-32B shape (8 agents, 64 layers, 64/8 heads, d 128).
 
@@ -752,7 +869,7 @@ def comix_bench():
             ref = torch.empty_like(out)
             wsb = max(pk.agent_decode_attention(pools, q[0], out, 0),
                       pk.agent_decode_attention(empty, q[0], ref, 0, wk, wv, [S] * A))
-            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
             rel_sum = torch.zeros((A, L), dtype=torch.float64, device=dev)
             abs_sum = torch.zeros((A, L), dtype=torch.float64, device=dev)
             for r in range(R):

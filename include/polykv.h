@@ -47,7 +47,10 @@ enum {
     PKV_EHIP = -5           /* a kernel launch failed (hipGetLastError) */
 };
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* Element types.  The type is a plain 32-bit integer so that any value a caller passes can be
+ * read and rejected (PKV_EUNSUPPORTED); an enum type would not hold values outside its list. */
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+typedef int32_t pkv_dtype;
 
 /* Shape of one pool.  K always uses 8 bits; V uses v_bits[l] bits in layer l.
  * v_signs: the V rotation's sign mask, bit i (little-endian over the 16 bytes)

@@ -135,3 +135,85 @@ def block_cost(n_tokens: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
     """
     return np.array([n_tokens * (n_kv_heads * (head_dim + head_dim * b // 8 + 4) + 4) for b in (2, 3, 4)],
                     dtype=np.uint64)
+
+
+class RefreshCycle:
+    """The controller's budget bookkeeping over agent starts, exits and refreshes.
+
+    CoMixKV news article, "online sensitivity estimation" paragraphs: the
+    controller weighs the sensitivities, the capacity each agent still has to
+    quantise and the real byte costs, chooses widths within the total budget,
+    recomputes the choice when an agent starts or ends and when new
+    observations arrive, and the budget an exiting agent held becomes
+    available to the others; "incremental quantization strategy": a block,
+    once quantised, keeps its encoding.  The readings taken here:
+
+    * one byte budget covers every resident agent's quantised blocks;
+    * each agent declares at start how many tokens it may quantise in all
+      (its capacity); what it has not yet quantised is its remaining capacity;
+    * a refresh has one item per (agent with remaining capacity, layer),
+      ordered by agent id then layer; an item at b bits costs what the
+      agent's remaining tokens take in that layer at b bits
+      (``block_cost(remaining, ...)``); the budget for the items is the total
+      minus the bytes the resident agents' stored blocks hold;
+    * the chosen widths apply to the agent's next block (a commit of up to
+      its remaining tokens); a stored block keeps its widths and bytes until
+      its agent exits;
+    * an exit releases that agent's blocks and its remaining capacity;
+    * an agent with no sensitivity given (it has seen nothing yet) counts 0.
+    """
+
+    def __init__(self, budget: int, n_layers: int, n_kv_heads: int, head_dim: int):
+        self.budget = int(budget)
+        self.n_layers, self.n_kv_heads, self.head_dim = n_layers, n_kv_heads, head_dim
+        self.capacity: dict[int, int] = {}
+        self.blocks: dict[int, list[tuple[int, np.ndarray]]] = {}  # agent -> [(tokens, bits [L])]
+
+    def start(self, agent: int, capacity_tokens: int) -> None:
+        if agent in self.blocks or capacity_tokens < 1:
+            raise ValueError("agent already resident, or no capacity")
+        self.capacity[agent] = int(capacity_tokens)
+        self.blocks[agent] = []
+
+    def exit(self, agent: int) -> int:
+        """Release the agent, its blocks and its remaining capacity; returns the stored bytes freed."""
+        freed = sum(self.block_bytes(n, b) for n, b in self.blocks.pop(agent))
+        del self.capacity[agent]
+        return int(freed)
+
+    def block_bytes(self, n_tokens: int, bits) -> int:
+        c = block_cost(n_tokens, self.n_kv_heads, self.head_dim)
+        return int(sum(int(c[b - 2]) for b in bits))
+
+    def stored_bytes(self) -> int:
+        return int(sum(self.block_bytes(n, b) for blocks in self.blocks.values() for n, b in blocks))
+
+    def remaining(self, agent: int) -> int:
+        return self.capacity[agent] - sum(n for n, _ in self.blocks[agent])
+
+    def refresh(self, sens: dict) -> dict | None:
+        """Widths of the next block of every resident agent with remaining capacity
+        ({agent: [L] bits}), or None when 2 bits everywhere does not fit."""
+        agents = [a for a in sorted(self.blocks) if self.remaining(a) > 0]
+        L = self.n_layers
+        if not agents:
+            return {}
+        s = np.concatenate([np.asarray(sens.get(a, np.zeros(L)), dtype=np.float32).reshape(L) for a in agents])
+        cost = np.concatenate([np.tile(block_cost(self.remaining(a), self.n_kv_heads, self.head_dim), (L, 1))
+                               for a in agents])
+        free = self.budget - self.stored_bytes()
+        if free < 0:
+            return None
+        bits = allocate(s, cost, error_factors(), free)
+        if bits is None:
+            return None
+        return {a: bits[i * L:(i + 1) * L] for i, a in enumerate(agents)}
+
+    def commit(self, widths: dict, n_tokens: int) -> None:
+        """Store the next block of n_tokens of each agent in widths, at those widths."""
+        for a, bits in widths.items():
+            if a not in self.blocks or not 0 < n_tokens <= self.remaining(a):
+                raise ValueError("agent not resident, or block beyond its remaining capacity")
+            self.blocks[a].append((int(n_tokens), np.asarray(bits, dtype=np.int64).copy()))
+        if self.stored_bytes() > self.budget:
+            raise ValueError("blocks exceed the budget")

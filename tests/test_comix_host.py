@@ -82,3 +82,65 @@ def test_sensitivity_validation_runs_on_host():
     assert call(win_k=0x2008) == -1                                    # window rows read in 16-byte pieces
     assert call(q=None) == -1 and call(out=None) == -1
     assert call(win_k=None) == -1
+
+
+def test_refresh_cycle_equals_oracle_at_qwen3_32b_shape():
+    """A refresh cycle on the Qwen3-32B controller shape (8 agents x 64 layers = 512 items,
+    8 kv heads, d 128, 1024 tokens of capacity per agent, 256-token blocks).
+
+    The caller's side keeps its own books (stored blocks, remaining capacity) and calls
+    comix_allocate_bits with item costs for each agent's remaining tokens and the budget left
+    by the stored blocks; at every refresh the widths equal the oracle's.  After an exit the
+    remaining agents' next blocks get the freed bytes (no item narrower than without the exit,
+    more bytes in total); stored blocks keep their widths.  Also times the allocation at 512
+    items."""
+    import time
+
+    A, L, Hkv, d, cap, n = 8, 64, 8, 128, 1024, 256
+
+    def row(tokens):  # bytes of one layer of `tokens` tokens at 2, 3, 4 bits (header layout)
+        return [tokens * (Hkv * (d + d * b // 8 + 4) + 4) for b in (2, 3, 4)]
+
+    err = [pk.lloyd_max_distortion(b) ** 0.5 for b in (2, 3, 4)]
+    budget = A * L * row(cap)[1]  # 3 bits on average over every agent's capacity
+    ref = comixkv.RefreshCycle(budget, L, Hkv, d)
+    stored = {}  # agent -> list of per-layer widths of its 256-token blocks
+    rng = np.random.default_rng(7)
+    for a in range(A):
+        ref.start(a, cap)
+        stored[a] = []
+    times = []
+
+    def refresh(sens):
+        agents = [a for a in sorted(stored) if len(stored[a]) * n < cap]
+        held = sum(row(n)[b - 2] for a in stored for blk in stored[a] for b in blk)
+        s = np.concatenate([sens[a] for a in agents]).astype(np.float32)
+        cost = [row(cap - len(stored[a]) * n) for a in agents for _ in range(L)]
+        t0 = time.perf_counter()
+        bits = pk.comix_allocate_bits(s, cost, err, budget - held)
+        times.append(time.perf_counter() - t0)
+        got = {a: bits[i * L:(i + 1) * L] for i, a in enumerate(agents)}
+        want = ref.refresh({a: sens[a] for a in agents})
+        assert {a: [int(x) for x in v] for a, v in want.items()} == got
+        return got
+
+    for _ in range(2):
+        sens = {a: rng.lognormal(0.0, 1.0, L).astype(np.float32) for a in stored}
+        w = refresh(sens)
+        ref.commit(w, n)
+        for a, b in w.items():
+            stored[a].append(list(b))
+    snapshot = {a: [list(b) for b in bl] for a, bl in stored.items()}
+    sens = {a: rng.lognormal(0.0, 1.0, L).astype(np.float32) for a in stored}
+    without_exit = refresh(sens)
+    # agent 5 exits: its two blocks' bytes and its remaining capacity are released
+    freed = ref.exit(5)
+    assert freed == sum(row(n)[b - 2] for blk in stored.pop(5) for b in blk)
+    with_exit = refresh(sens)
+    assert sorted(with_exit) == [a for a in range(A) if a != 5]
+    assert all(x >= y for a in with_exit for x, y in zip(with_exit[a], without_exit[a]))
+    assert sum(with_exit[a].count(4) for a in with_exit) > sum(without_exit[a].count(4) for a in with_exit)
+    assert all(stored[a] == snapshot[a] for a in stored)
+    # a refresh at 512 items is host work of well under a millisecond; bound it loosely
+    print(f"comix_allocate_bits at {A * L} items: median {1e6 * np.median(times):.0f} us")
+    assert np.median(times) < 0.05

@@ -125,3 +125,104 @@ def test_controller_end_to_end_matches_oracle():
     assert int(cost[np.arange(s_dev.size), np.array(bits) - 2].sum()) <= budget
     assert comixkv.objective(s_ref, comixkv.error_factors(), bits) <= comixkv.objective(
         s_ref, comixkv.error_factors(), [3] * s_dev.size) + 1e-12
+
+
+def test_refresh_cycle_end_to_end():
+    """A CoMixKV refresh cycle on the device: three agents quantise their first 64-token
+    blocks at widths chosen from device sensitivities; one exits; the two left refresh on
+    their newer windows and quantise their second blocks, which get the freed bytes.
+
+    Checked: widths equal the oracle's refresh cycle on the same sensitivities; every block's
+    image equals the oracle's encoding byte for byte; the first blocks' bytes do not change
+    when the second blocks are written; the second widths are no narrower than the same
+    refresh without the exit; decoding each agent over its two blocks (first as its pool,
+    second as its private pool) plus its last 32 native tokens matches the fp64 oracle.
+    """
+    from oracle import attention, pool_image
+
+    import gpu_helpers as h
+
+    print("[comix] refresh cycle", flush=True)
+    w = wl.LLAMA3_8B.replace(n_layers=4, n_kv_heads=2, n_q_heads=8, n_agents=3, sfx_tokens=160)
+    A, L, Hkv, Hq, d = w.n_agents, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    blk, cap, win, R = 64, 128, 96, 2
+    q, k_all, v_all = _inputs(w, R, "bf16")
+    err = [pk.lloyd_max_distortion(b) ** 0.5 for b in (2, 3, 4)]
+
+    def row(tokens):
+        return [tokens * (Hkv * (d + d * b // 8 + 4) + 4) for b in (2, 3, 4)]
+
+    budget = int(0.93 * A * L * row(cap)[1])
+    cycle = comixkv.RefreshCycle(budget, L, Hkv, d)
+    for a in range(A):
+        cycle.start(a, cap)
+
+    def sensitivities(agents, t0):
+        out = torch.empty((len(agents), L), dtype=torch.float32, device=DEV)
+        pk.comix_sensitivity(q[:, agents].contiguous(), k_all[agents, :, :, t0:t0 + win].contiguous(),
+                             v_all[agents, :, :, t0:t0 + win].contiguous(), [win] * len(agents), out)
+        torch.cuda.synchronize()
+        return {a: out[i].cpu().numpy() for i, a in enumerate(agents)}
+
+    def allocate(agents, sens, done, held):
+        s = np.concatenate([sens[a] for a in agents]).astype(np.float32)
+        bits = pk.comix_allocate_bits(s, [row(cap - done)] * s.size, err, budget - held)
+        return {a: bits[i * L:(i + 1) * L] for i, a in enumerate(agents)}
+
+    def quantize(a, bits, t0):
+        dp = h.DevicePool(L, Hkv, d, blk, bits)
+        dp.append(0, k_all[a, :, :, t0:t0 + blk].contiguous(), v_all[a, :, :, t0:t0 + blk].contiguous())
+        ref = pool_image.PoolImage(L, Hkv, d, blk, bits)
+        ref.append(0, k_all[a, :, :, t0:t0 + blk].float().cpu().numpy(),
+                   v_all[a, :, :, t0:t0 + blk].float().cpu().numpy())
+        assert all(x == 0 for x in h.compare_image(dp, ref).values()), (a, t0)
+        return dp, ref
+
+    # refresh 1: all three agents, windows [0, 96)
+    sens = sensitivities([0, 1, 2], 0)
+    w1 = allocate([0, 1, 2], sens, 0, 0)
+    assert {a: [int(x) for x in b] for a, b in cycle.refresh(sens).items()} == w1
+    cycle.commit(w1, blk)
+    first = {a: quantize(a, w1[a], 0) for a in range(A)}
+    snap = {a: first[a][0].host_bytes().copy() for a in range(A)}
+    held = sum(row(blk)[b - 2] for a in range(A) for b in w1[a])
+    # agent 2 exits
+    freed = cycle.exit(2)
+    assert freed == sum(row(blk)[b - 2] for b in w1[2])
+    del first[2]
+    # refresh 2: agents 0 and 1 on windows [64, 160)
+    sens = sensitivities([0, 1], blk)
+    w2 = allocate([0, 1], sens, blk, held - freed)
+    assert {a: [int(x) for x in b] for a, b in cycle.refresh(sens).items()} == w2
+    # the same refresh without the exit: agent 2's block and remaining capacity still counted
+    sens_x = dict(sens)
+    sens_x[2] = np.zeros(L, dtype=np.float32)
+    no_exit = allocate([0, 1, 2], sens_x, blk, held)
+    assert all(x >= y for a in (0, 1) for x, y in zip(w2[a], no_exit[a]))
+    assert sum(w2[a].count(4) for a in (0, 1)) > sum(no_exit[a].count(4) for a in (0, 1))
+    cycle.commit(w2, blk)
+    second = {a: quantize(a, w2[a], blk) for a in (0, 1)}
+    for a in (0, 1):
+        assert np.array_equal(first[a][0].host_bytes(), snap[a]), a
+    assert [[list(b) for _, b in cycle.blocks[a]] for a in (0, 1)] == [[list(w1[a]), list(w2[a])] for a in (0, 1)]
+
+    # decode: each agent over its two blocks and its last 32 native tokens
+    agents = [0, 1]
+    S = 160 - cap
+    qd = q[-1, agents].contiguous()
+    sk = k_all[agents, :, :, cap:].contiguous()
+    sv = v_all[agents, :, :, cap:].contiguous()
+    out = torch.full(tuple(qd.shape), float("nan"), dtype=torch.float32, device=DEV)
+    pools = [first[a][0].pool for a in agents]
+    prv = [second[a][0].pool for a in agents]
+    wsb = pk.agent_decode_attention(pools, qd, out, 0, sk, sv, [S] * 2, private_pools=prv)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+    pk.agent_decode_attention(pools, qd, out, 0, sk, sv, [S] * 2, workspace=ws, private_pools=prv)
+    torch.cuda.synchronize()
+    skh, svh = sk.float().cpu().numpy(), sv.float().cpu().numpy()
+    want = attention.decode_call(
+        qd.float().cpu().numpy(), [0, 1], lambda p, l, g: first[agents[p]][1].decoded_layer(l, g),
+        lambda i, l: skh[i, l], lambda i, l: svh[i, l], [S] * 2, Hkv,
+        private=lambda i, l, g: second[agents[i]][1].decoded_layer(l, g))
+    e = attention.max_rel_error(out.cpu().numpy().astype(np.float64), want)
+    assert e <= 1e-3, e

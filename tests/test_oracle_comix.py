@@ -177,3 +177,83 @@ def test_block_cost_matches_pool_layout_bytes_per_token():
     # 180 B per (token, kv head) at d 128 and 3 bits, plus 4 B of K scale per token
     assert list(comixkv.block_cost(1, 1, 128)) == [128 + 32 + 4 + 4, 128 + 48 + 4 + 4, 128 + 64 + 4 + 4]
     assert comixkv.block_cost(4096, 8, 128)[1] == 4096 * (8 * 180 + 4)
+
+
+# ---------------------------------------------------------------- refresh cycle
+def _widths(w):
+    return {a: [int(x) for x in b] for a, b in w.items()}
+
+
+def test_refresh_cycle_hand_worked():
+    """A start -> refresh -> commit -> exit -> refresh sequence worked by hand.
+
+    Two layers, one kv head, d = 64: a token of one layer takes 64 + 64 b / 8 + 4 + 4 bytes,
+    88 / 96 / 104 at 2 / 3 / 4 bits.  Two agents of 16 tokens capacity each, budget 5988.
+    Error decreases per unit of sensitivity: e2 - e3 = 0.15689, e3 - e4 = 0.08840.
+    """
+    rc = comixkv.RefreshCycle(5988, 2, 1, 64)
+    rc.start(0, 16)
+    rc.start(1, 16)
+    sens = {0: [4.0, 1.0], 1: [2.0, 3.0]}
+    # 16 remaining tokens per item: 1408 / 1536 / 1664, upgrades of 128.  2 bits everywhere:
+    # 5632 of 5988, 356 spare.  Gains: (0,0) 2->3 0.628, (1,1) 2->3 0.471 fit (100 left);
+    # (0,0) 3->4 0.354 and every later one need 128: frozen.
+    w = rc.refresh(sens)
+    assert _widths(w) == {0: [3, 2], 1: [2, 3]}
+    rc.commit(w, 8)  # the first 8-token blocks: 768 + 704 bytes each
+    assert rc.stored_bytes() == 2944 and rc.remaining(0) == rc.remaining(1) == 8
+    # 8 remaining tokens per item: 704 / 768 / 832, upgrades of 64; 3044 free, 2816 at 2 bits,
+    # 228 spare: (0,0) 0.628 -> 164, (1,1) 0.471 -> 100, (0,0) 3->4 0.354 -> 36; (1,0) 0.314 frozen
+    assert _widths(rc.refresh(sens)) == {0: [4, 2], 1: [2, 3]}
+    # agent 1 exits: its block and its remaining capacity go; agent 0 alone has 1408 at 2 bits
+    # against 4516 free: every upgrade fits
+    assert rc.exit(1) == 1472
+    assert rc.stored_bytes() == 1472
+    w = rc.refresh(sens)
+    assert _widths(w) == {0: [4, 4]}
+    rc.commit(w, 8)
+    assert [(n, list(b)) for n, b in rc.blocks[0]] == [(8, [3, 2]), (8, [4, 4])]
+    assert rc.stored_bytes() == 1472 + 1664 and rc.remaining(0) == 0
+    # a full agent has no items; a new one of 32 tokens needs 5632 at 2 bits against 2852 free
+    assert rc.refresh(sens) == {}
+    rc.start(2, 32)
+    assert rc.refresh(sens) is None
+    assert rc.exit(0) == 3136
+    # zero sensitivity: every gain is 0 and ties; the rule still takes an upgrade that fits,
+    # lowest index first: 5632 at 2 bits, 356 spare, upgrades of 256 -> one
+    assert _widths(rc.refresh({})) == {2: [3, 2]}
+
+
+def test_refresh_cycle_orders_items_by_agent_id():
+    """One upgrade fits and every gain ties: it goes to the lowest agent id's first layer,
+    whatever order the agents started in."""
+    rc = comixkv.RefreshCycle(2816 + 64 + 10, 2, 1, 64)
+    rc.start(5, 8)
+    rc.start(3, 8)
+    w = rc.refresh({5: [1.0, 1.0], 3: [1.0, 1.0]})
+    assert _widths(w) == {3: [3, 2], 5: [2, 2]}
+
+
+def test_refresh_cycle_stored_blocks_keep_their_widths():
+    """Refreshes and commits never change a stored block; an exit frees exactly its blocks;
+    stored bytes never exceed the budget."""
+    rng = np.random.default_rng(3)
+    L = 4
+    rc = comixkv.RefreshCycle(5 * L * 640 * (8 * (128 + 48 + 4) + 4), L, 8, 128)  # 3 bits on average
+    for a in range(5):
+        rc.start(a, 640)
+    history = []
+    for step in range(6):
+        w = rc.refresh({a: rng.lognormal(0, 1, L) for a in rc.blocks})
+        assert w is not None
+        rc.commit(w, 64)
+        assert rc.stored_bytes() <= rc.budget
+        history.append({a: [(n, b.copy()) for n, b in bl] for a, bl in rc.blocks.items()})
+        for past in history:
+            for a, bl in past.items():
+                if a in rc.blocks:
+                    assert all(n == m and np.array_equal(x, y) for (n, x), (m, y) in zip(bl, rc.blocks[a]))
+        if step == 2:
+            want = sum(rc.block_bytes(n, b) for n, b in rc.blocks[1])
+            before = rc.stored_bytes()
+            assert rc.exit(1) == want and rc.stored_bytes() == before - want
