@@ -368,6 +368,25 @@ struct StageLayout {
     static_assert(NOFF + 256 <= Ring<D>::kStageBytes, "stage overflow");
 };
 
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Scheduling groups for the compiler (no instructions): N times one matrix-core instruction
+// followed by V vector instructions, so the two units work side by side
+template <int N, int V>
+__device__ __forceinline__ void interleave() {
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+        interleave<N - 1, V>();
+    }
+}
+
 // Always inlined: an out-of-line body would receive the launch struct by reference,
 // which makes every lane copy it to scratch.
 template <int D, int RT, int BITS, bool QSPLIT>
@@ -377,6 +396,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     constexpr int KS = D / 32;   // QK k-steps
     constexpr int DL = D / 4;    // K bytes per lane per token
     constexpr int CB = SL::CB;   // V code bytes per lane per step
+    constexpr int kQK = 2 * KS * (QSPLIT ? 2 : 1);  // matrix-core instructions of one tile's scores
+    constexpr int kPV = 2 * NB;                     // ... and of one tile's P.V products (hi + lo)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -462,8 +483,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
 
     // ---- set-up loads first, all at once: this lane's query chunks (8 values per
     // (row tile, k-step): one 16-byte load for bf16, two for fp32) and one codebook
-    // entry per lane; then the ring, so that waiting for the set-up loads does not
-    // wait for the ring
+    // entry per lane; the ring's loads follow the query conversion
     constexpr int QV = QSPLIT ? 2 : 1;
     // hi + lo query operands (QSPLIT) for fp32 queries, and for bf16 queries that carry a
     // per-channel pool's K scales
@@ -516,10 +536,6 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
     }
     const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x
-
-#pragma unroll
-    for (int it = 0; it < RG::kStages - 1; ++it)
-        if (it < my_steps) issue(it);
 
     // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i).
     // Each row is first multiplied by 2^-e, e = max(0, E - 15) with max|q| < 2^E, so every
@@ -590,6 +606,11 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
     // every wavefront of the workgroup holds all rows, so they all take the same branch below
     const bool scaled_rows = __builtin_amdgcn_ballot_w64(any_scaled) != 0ull;
+    // the ring's first steps: issued once the query loads have landed, so those do not queue
+    // behind the ring's burst of loads
+#pragma unroll
+    for (int it = 0; it < RG::kStages - 1; ++it)
+        if (it < my_steps) issue(it);
     if constexpr (BITS == 3) {
         // LUT of fp16 centroid quads: entry e = c0 | c1 << 3 | c2 << 6 | c3 << 9 ->
         // (c[c0], c[c1], c[c2], c[c3]); this thread's entries tid + 256 k share the low pair
@@ -724,6 +745,37 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
     }
 
+    // P.V of row tile rt with the weights (hi, lo): the eight hi products first, then the
+    // lo ones, so no product waits for the one before it
+    auto pv = [&](const half8 (&vb)[NB], int rt, const H8& wh, const H8& wl) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh.h, vb[nb], acc[rt][nb], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl.h, vb[nb], acc[rt][nb], 0, 0, 0);
+    };
+    // softmax of row tile rt from its scores: exponents, row sum, running max, and the
+    // weights w = p' * vn as fp16 hi + lo (w - hi, rounded once more): ~2^-22 relative
+    auto weights = [&](const f32x4 (&S)[2], int rt, const float (&nn)[8], const float (&ff)[8], const bool (&ok)[8],
+                       auto tail_tag, H8& wh, H8& wl) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = fmaf(S[i >> 2][i & 3], ff[i], cref[rt]);
+            if (TAIL) x[i] = ok[i] ? x[i] : -INFINITY;
+        }
+        xmax[rt] = max3(max3(xmax[rt], x[0], x[1]), max3(x[2], x[3], x[4]), max3(x[5], x[6], x[7]));
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(x[i]);
+            const float p1 = __builtin_amdgcn_exp2f(x[i + 1]);
+            lsum[rt] += p0 + p1;
+            weights_hilo(p0, nn[i], p1, nn[i + 1], wh.u[i / 2], wl.u[i / 2]);
+        }
+    };
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -737,81 +789,103 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             for (int it = 0; it < RG::kStages - 1; ++it)
                 if (it < my_steps) issue(it);
         }
-        // One 32-token step.  The ring reads of the next step are issued once this
-        // step's last LDS reads (the LUT) have completed, and land while the softmax and
-        // the P.V products run: nothing else reads LDS in between.  TAIL masks tokens at
-        // or past the end of the split.
-        // One 32-token step from the registers of `raw`, which then receive the next
-        // step's ring contents: those reads are issued once this step's own LDS reads
-        // (the LUT) have completed, and land while the softmax and the P.V products run
-        // (nothing else reads LDS in between).  TAIL masks tokens at or past the end of
-        // the split.
-        auto step = [&](const int it, Raw& raw, auto tail_tag, const bool prefetch) {
-            constexpr bool TAIL = decltype(tail_tag)::value;
-            const int t0 = tb + (wave + it * kWaves) * kStep;
-            if (prefetch) {
-                if (it + RG::kStages - 1 < my_steps) issue(it + RG::kStages - 1);  // slot of step it - 1, already read
-                wait_groups(min(RG::kStages - 2, my_steps - 2 - it));       // loads of step it + 1 landed
-            }
-            Chunk<CB> ch;
-            raw.code_words(ch.w);
-            // V centroids for the 8 tokens x NB dims of this lane, from the LUT
-            half8 vb[NB];
-            decode_all<CB, BITS>(vb, ch, lut_lane);
-            half8 ka[2][KS];
-            convert_k(raw, ka);
-            float nn[8], ff[8];
-            norms(raw.ns, nn, ff);
-            bool ok[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                ok[i] = !TAIL || (t0 + 8 * lg + i < te);
-                if (TAIL) nn[i] = ok[i] ? nn[i] : 0.0f;
-            }
-            // scores of the first row tile while the LUT reads complete
-            f32x4 S[2];
-            scores(ka, 0, S);
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LUT values in registers
-            __builtin_amdgcn_sched_barrier(0);
-            if (prefetch) ring_issue(it + 1, raw);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    x[i] = fmaf(S[i >> 2][i & 3], ff[i], cref[rt]);
-                    if (TAIL) x[i] = ok[i] ? x[i] : -INFINITY;
-                }
-                // the next row tile's scores overlap this tile's softmax
-                if (rt + 1 < RT) scores(ka, rt + 1, S);
-                xmax[rt] = max3(max3(xmax[rt], x[0], x[1]), max3(x[2], x[3], x[4]), max3(x[5], x[6], x[7]));
-                // weights w = p' * vn as fp16 hi + lo (w - hi, rounded once more): ~2^-22 relative
-                H8 wh, wl;
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(x[i]);
-                    const float p1 = __builtin_amdgcn_exp2f(x[i + 1]);
-                    lsum[rt] += p0 + p1;
-                    weights_hilo(p0, nn[i], p1, nn[i + 1], wh.u[i / 2], wl.u[i / 2]);
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh.h, vb[nb], acc[rt][nb], 0, 0, 0);
-                    acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl.h, vb[nb], acc[rt][nb], 0, 0, 0);
-                }
-            }
-            if (prefetch) ring_fence(raw);
-        };
+        // The step loop is software-pipelined so that matrix-core and vector work of
+        // different stages overlap.  Entering step it, the K operands (ka), V centroids (vb),
+        // norms and score factors of step it are in registers and the scores of row tile 0
+        // are issued.  Then, per row tile rt, the softmax of rt runs beside the scores of
+        // rt + 1 and the P.V products of rt - 1; the last tile's P.V products run beside the
+        // conversion of step it + 1's K, and its V decode beside the first scores of it + 1.
+        // The ring reads of step it + 1 are issued before the last row tile's softmax and
+        // waited for before the K conversion.
+        // TAIL masks tokens at or past the end of the split; NEXT prepares step it + 1.
         const bool has_tail = my_steps > 0 && (te - tb) % kStep != 0 && wave == (nsteps - 1) % kWaves;
-        const int full = my_steps - (has_tail ? 1 : 0);
-        Raw raw;
         if (my_steps > 0) {
+            Raw raw;
+            half8 ka[2][KS];
+            half8 vb[NB];
+            float nn[8], ff[8];
+            f32x4 S0[2];
             wait_groups(min(my_steps - 1, RG::kStages - 2));
             ring_issue(0, raw);
             ring_fence(raw);
+            {
+                Chunk<CB> ch;
+                raw.code_words(ch.w);
+                decode_all<CB, BITS>(vb, ch, lut_lane);
+            }
+            convert_k(raw, ka);
+            norms(raw.ns, nn, ff);
+            scores(ka, 0, S0);
+            // WAITG: load groups (steps) allowed in flight once step it + 1 has landed; ISSUE: step
+            // it + kStages - 1 exists and is fetched now.  Both compile-time, so a step is one
+            // branch-free block for the scheduler.
+            auto step = [&](const int it, auto tail_tag, auto next_tag, auto waitg_tag, auto issue_tag) {
+                constexpr bool TAIL = decltype(tail_tag)::value;
+                constexpr bool NEXT = decltype(next_tag)::value;
+                constexpr int WAITG = decltype(waitg_tag)::value;
+                constexpr bool ISSUE = decltype(issue_tag)::value;
+                const int t0 = tb + (wave + it * kWaves) * kStep;
+                if constexpr (ISSUE) issue(it + RG::kStages - 1);  // into the slot of step it - 1, already read
+                bool ok[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ok[i] = !TAIL || (t0 + 8 * lg + i < te);
+                    if (TAIL) nn[i] = ok[i] ? nn[i] : 0.0f;
+                }
+                H8 wh[2], wl[2];  // weights of tiles rt (index rt & 1) and rt - 1
+                f32x4 S[2][2];    // scores of tiles rt and rt + 1 (index by parity)
+                S[0][0] = S0[0];
+                S[0][1] = S0[1];
+                // per row tile rt: its softmax beside the scores of rt + 1 and the P.V products of
+                // rt - 1 (all inputs produced before)
+                static_for<0, RT>([&](auto rt_tag) {
+                    constexpr int rt = decltype(rt_tag)::value;
+                    if constexpr (NEXT && rt == RT - 1) {
+                        // the ring reads of step it + 1 land during the last tile's softmax and
+                        // P.V products (issued this late so their registers are not held all step)
+                        wait_vmcnt<WAITG * SL::NDMA>();  // loads of step it + 1 landed
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LUT reads of this step are in
+                        ring_issue(it + 1, raw);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if constexpr (rt + 1 < RT) scores(ka, rt + 1, S[(rt + 1) & 1]);
+                    weights(S[rt & 1], rt, nn, ff, ok, tail_tag, wh[rt & 1], wl[rt & 1]);
+                    if constexpr (rt >= 1) pv(vb, rt - 1, wh[(rt - 1) & 1], wl[(rt - 1) & 1]);
+                });
+                if constexpr (NEXT) {
+                    __builtin_amdgcn_sched_barrier(0);  // the wait for the ring reads stays here
+                    ring_fence(raw);
+                    convert_k(raw, ka);
+                }
+                pv(vb, RT - 1, wh[(RT - 1) & 1], wl[(RT - 1) & 1]);
+                if constexpr (NEXT) {
+                    Chunk<CB> ch;
+                    raw.code_words(ch.w);
+                    decode_all<CB, BITS>(vb, ch, lut_lane);
+                    norms(raw.ns, nn, ff);
+                    scores(ka, 0, S0);
+                    // the last tile's products and the first scores of step it + 1 beside the K
+                    // conversion and V decode of step it + 1
+                    interleave<kPV + kQK, 5>();
+                }
+            };
+            using F = std::false_type;
+            using T = std::true_type;
+            using G0 = std::integral_constant<int, 0>;
+            using G1 = std::integral_constant<int, 1>;
+            using G2 = std::integral_constant<int, RG::kStages - 2>;
+            static_assert(RG::kStages == 3 || RG::kStages == 4, "ring depth");
+            // steady state: step it + 1 landed with kStages - 2 later steps in flight, and step
+            // it + kStages - 1 to fetch; then the last steps of the ring, and the final step
+            int it = 0;
+            for (; it + RG::kStages <= my_steps; ++it) step(it, F{}, T{}, G2{}, T{});
+            if constexpr (RG::kStages == 4) {
+                if (it + 3 == my_steps) step(it++, F{}, T{}, G1{}, F{});
+            }
+            if (it + 2 == my_steps) step(it++, F{}, T{}, G0{}, F{});
+            if (has_tail) step(my_steps - 1, T{}, F{}, G0{}, F{});
+            else step(my_steps - 1, F{}, F{}, G0{}, F{});
         }
-        for (int it = 0; it < full; ++it) step(it, raw, std::false_type{}, it + 1 < my_steps);
-        if (has_tail) step(full, raw, std::true_type{}, false);
         // any row over the limit? then every wave re-runs with the exact row maxima
         if (tid == 0) g_flag = 0;
         lds_barrier();
