@@ -1038,10 +1038,14 @@ __global__ void __launch_bounds__(256) k_sfx(DecodeLaunch a) {
 
 // One wavefront per output row (launch agent, layer, q head): combine the
 // pool's split records, apply the inverse FWHT (H / d) to the rotated-domain
-// accumulator, fold in the suffix record and normalise.
+// accumulator, fold in the suffix record and normalise.  The records' (m, l)
+// are spread over the lanes (record j on lane j % 64), so their loads are all in
+// flight at once; the accumulators are then summed eight records at a time,
+// their loads issued before any is used.
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     constexpr int EPL = D / 64;
+    constexpr int U = 8;  // records whose accumulator loads are in flight together
     const int lane = threadIdx.x & 63;
     const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const uint64_t n_rows = (uint64_t)a.n_agents * a.lc * a.hq;
@@ -1051,8 +1055,7 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     const int k = row / ((uint64_t)a.hq * a.lc);
     const int g = h / a.G;
     // the agent's pool and, if it has one, its private pool: split records of both, all in
-    // the rotated domain, merged before the one inverse transform
-    const int np = a.agent_pool2[k] >= 0 ? 2 : 1;
+    // the rotated domain, merged before the one inverse transform (records 0 .. n0-1 the pool's)
     auto records = [&](int which, const float*& rec0, uint64_t& stride, int& splits) {
         const PoolEntry& P = a.pools[which == 0 ? a.agent_pool[k] : a.agent_pool2[k]];
         const int rho = (which == 0 ? a.agent_pos[k] : a.agent_pos2[k]) * a.G + h % a.G;
@@ -1060,31 +1063,52 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
         stride = (uint64_t)P.rows * (2 + D);
         splits = P.splits;
     };
+    const float* base0;
+    const float* base1 = nullptr;
+    uint64_t st0, st1 = 0;
+    int n0, n1 = 0;
+    records(0, base0, st0, n0);
+    if (a.agent_pool2[k] >= 0) records(1, base1, st1, n1);
+    const int nrec = n0 + n1;
+    auto rec = [&](int j) { return j < n0 ? base0 + (uint64_t)j * st0 : base1 + (uint64_t)(j - n0) * st1; };
+    // M = max of the records' m; L = sum of 2^(m - M) l
     float M = -INFINITY;
-    for (int w = 0; w < np; ++w) {
-        const float* rec0;
-        uint64_t stride;
-        int splits;
-        records(w, rec0, stride, splits);
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, rec0[s * stride]);
-    }
+    for (int j = lane; j < nrec; j += 64) M = fmaxf(M, rec(j)[0]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     float L = 0.0f, z[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
     if (M != -INFINITY) {
-        for (int w = 0; w < np; ++w) {
-            const float* rec0;
-            uint64_t stride;
-            int splits;
-            records(w, rec0, stride, splits);
-            for (int s = 0; s < splits; ++s) {
-                const float* r = rec0 + s * stride;
-                const float wt = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
+        for (int c = 0; c < nrec; c += 64) {
+            // this lane's record c + lane: its weight (0 past the end and for empty records)
+            float wt = 0.0f;
+            if (c + lane < nrec) {
+                const float* r = rec(c + lane);
+                const float m = r[0];
+                wt = (m == -INFINITY) ? 0.0f : exp2f(m - M);
                 L += wt * r[1];
+            }
+            const int nc = min(64, nrec - c);
+            for (int j0 = 0; j0 < nc; j0 += U) {
+                float v[U][EPL];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) z[e] += wt * r[2 + EPL * lane + e];
+                for (int u = 0; u < U; ++u) {
+                    const int j = c + min(j0 + u, nc - 1);  // past the end: a valid record, weight 0
+                    const float* r = rec(j) + 2 + EPL * lane;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) v[u][e] = r[e];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float w = j0 + u < nc ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j0 + u)) : 0.0f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) z[e] = fmaf(w, v[u][e], z[e]);
+                }
             }
         }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off, 64);
     }
     // inverse transform: H z / D (lane holds dims EPL*lane + e), then the rotation's signs
     if (EPL == 2) {
