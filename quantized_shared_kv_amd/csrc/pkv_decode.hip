@@ -472,7 +472,7 @@ __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int D, int RS>
+template <int D, int RS, bool PF>
 __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
     // score sweep: LPT lanes per token, each reading KL 16-byte chunks of it (and holding the
     // matching query slices: RS * KL * 4 registers)
@@ -550,14 +550,30 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
             float mloc[RPL];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) mloc[i] = -INFINITY;
-            for (int g0 = 0; g0 < nc; g0 += KG) {
-                uint4 kk[KU][KL];
+            // PF: each group's K loads are issued one group ahead (the next group's while this one
+            // is scored), so a wave waits for one load latency per chunk, not one per group (for
+            // launches too small to hide the latency with other waves; it costs registers)
+            uint4 kn[KU][KL];
+            auto load_k = [&](uint4 (&dst)[KU][KL], int gs) {
 #pragma unroll
                 for (int u = 0; u < KU; ++u) {
-                    const int t = min(g0 + u * TPP + tl, nc - 1);  // past the chunk: a valid token, score dropped
+                    const int t = min(gs + u * TPP + tl, nc - 1);  // past the chunk: a valid token, score dropped
                     const uint32_t off = (uint32_t)t * (D * 2) + (uint32_t)part * 16;
 #pragma unroll
-                    for (int c = 0; c < KL; ++c) kk[u][c] = ld16(Kc, off + c * LPT * 16);
+                    for (int c = 0; c < KL; ++c) dst[u][c] = ld16(Kc, off + c * LPT * 16);
+                }
+            };
+            if constexpr (PF) load_k(kn, 0);
+            for (int g0 = 0; g0 < nc; g0 += KG) {
+                uint4 kk[KU][KL];
+                if constexpr (PF) {
+#pragma unroll
+                    for (int u = 0; u < KU; ++u)
+#pragma unroll
+                        for (int c = 0; c < KL; ++c) kk[u][c] = kn[u][c];
+                    load_k(kn, g0 + KG);
+                } else {
+                    load_k(kk, g0);
                 }
 #pragma unroll
                 for (int u = 0; u < KU; ++u) {
@@ -619,6 +635,16 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
                 for (int e = 0; e < 8; ++e) acc[r * 8 + e] *= alpha;
             }
             __builtin_amdgcn_wave_barrier();
+            // PF: the first value group's loads (they do not depend on the scores)
+            uint4 vn[VU];
+            auto load_v = [&](uint4 (&dst)[VU], int gs) {
+#pragma unroll
+                for (int u = 0; u < VU; ++u) {
+                    const int t = min(gs + u * TV + tv, nc - 1);  // past the chunk: a valid token, weight 0
+                    dst[u] = ld16(Vc, (uint32_t)t * (D * 2) + (uint32_t)dv * 16);
+                }
+            };
+            if constexpr (PF) load_v(vn, 0);
             // ---- probabilities in place, per-lane partial sums
             for (int t = lane; t < nc; t += 64) {
 #pragma unroll
@@ -629,13 +655,15 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
                 }
             }
             __builtin_amdgcn_wave_barrier();
-            // ---- 2. values
+            // ---- 2. values (PF: loads one group ahead, as the keys)
             for (int g0 = 0; g0 < nc; g0 += VG) {
                 uint4 vv[VU];
+                if constexpr (PF) {
 #pragma unroll
-                for (int u = 0; u < VU; ++u) {
-                    const int t = min(g0 + u * TV + tv, nc - 1);  // past the chunk: a valid token, weight 0
-                    vv[u] = ld16(Vc, (uint32_t)t * (D * 2) + (uint32_t)dv * 16);
+                    for (int u = 0; u < VU; ++u) vv[u] = vn[u];
+                    load_v(vn, g0 + VG);
+                } else {
+                    load_v(vv, g0);
                 }
 #pragma unroll
                 for (int u = 0; u < VU; ++u) {
@@ -715,13 +743,13 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
 }
 
 // grid ceil(n_agents * lc * hkv / 4), 256 threads = 4 wavefronts, one unit each
-template <int D, int RS>
+template <int D, int RS, bool PF>
 __global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
     __shared__ __align__(16) float sbuf[4][kSfxChunk * RS];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int unit = blockIdx.x * 4 + wave;
     if (unit >= a.n_agents * a.lc * a.hkv) return;
-    sfx_fast_wave<D, RS>(a, unit, sbuf[wave]);
+    sfx_fast_wave<D, RS, PF>(a, unit, sbuf[wave]);
 }
 
 // ------------------------------------------------------------------ private segments
@@ -1417,6 +1445,14 @@ int validate(const pkv_decode_args* x) {
     return PKV_OK;
 }
 
+template <int D, bool PF>
+void launch_sfx_fast(const DecodeLaunch& L, dim3 grid, hipStream_t s) {
+    if (L.G == 1) hipLaunchKernelGGL((k_sfx_fast<D, 1, PF>), grid, dim3(kThreads), 0, s, L);
+    else if (L.G == 2) hipLaunchKernelGGL((k_sfx_fast<D, 2, PF>), grid, dim3(kThreads), 0, s, L);
+    else if (L.G <= 4) hipLaunchKernelGGL((k_sfx_fast<D, 4, PF>), grid, dim3(kThreads), 0, s, L);
+    else hipLaunchKernelGGL((k_sfx_fast<D, 8, PF>), grid, dim3(kThreads), 0, s, L);
+}
+
 template <int D>
 int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hipStream_t s) {
     Centroids cents;
@@ -1428,11 +1464,11 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
             const int units = L.n_agents * L.lc * L.hkv;
             const dim3 grid((units + 3) / 4);
             if (L.q_dtype == PKV_BF16 && L.sfx_dtype == PKV_BF16) {
-                // rows per pass: the group size rounded up to a power of two, at most 8
-                if (L.G == 1) hipLaunchKernelGGL((k_sfx_fast<D, 1>), grid, dim3(kThreads), 0, s, L);
-                else if (L.G == 2) hipLaunchKernelGGL((k_sfx_fast<D, 2>), grid, dim3(kThreads), 0, s, L);
-                else if (L.G <= 4) hipLaunchKernelGGL((k_sfx_fast<D, 4>), grid, dim3(kThreads), 0, s, L);
-                else hipLaunchKernelGGL((k_sfx_fast<D, 8>), grid, dim3(kThreads), 0, s, L);
+                // rows per pass: the group size rounded up to a power of two, at most 8; with fewer
+                // waves than SIMDs (e.g. a single-layer call) latency rules, so each wave keeps its
+                // next load group in flight; with more, other waves hide it at the lower register count
+                if (units < 1024) launch_sfx_fast<D, true>(L, grid, s);
+                else launch_sfx_fast<D, false>(L, grid, s);
             } else {
                 hipLaunchKernelGGL(k_sfx<D>, grid, dim3(kThreads), 0, s, L);
             }
