@@ -389,7 +389,10 @@ __device__ __forceinline__ void interleave() {
 
 // Always inlined: an out-of-line body would receive the launch struct by reference,
 // which makes every lane copy it to scratch.
-template <int D, int RT, int BITS, bool QSPLIT>
+// FUSED: every (layer, kv head) is one workgroup, which finishes its rows itself; otherwise the
+// workgroup writes partial records for k_merge.  Separate instantiations, so neither form's code
+// shapes the other's register allocation.
+template <int D, int RT, int BITS, bool QSPLIT, bool FUSED>
 __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const CentArg& cents) {
     using SL = StageLayout<D, BITS>;
     constexpr int NB = D / 16;   // PV column tiles
@@ -927,7 +930,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     constexpr int RPW = kMaxRows / kWaves;  // rows finished per wavefront
     constexpr int FD = D / 16;              // fused finish: dimensions per lane (16 lanes per row)
     constexpr int FI = RPW / 4;             // fused finish: rows per lane (4 rows per wavefront pass)
-    const bool fused = a.fused != 0;
+    constexpr bool fused = FUSED;
     // fused finish: lane (fq, fl) handles rows wave + kWaves * (4 i + fq), i < FI, dims
     // FD fl .. FD fl + FD - 1.  Its rows' agents, heads and suffix records are fetched
     // now, so their latency overlaps the combine
@@ -935,7 +938,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     float su_m[FI], su_l[FI], su_v[FI][FD];
     float se_m[FI], se_l[FI], se_v[FI][FD];  // the agent's private segment record (rotated domain), if any
     int f_row[FI], f_head[FI], f_agent[FI];
-    if (fused) {
+    if constexpr (fused) {
         const float rG = __builtin_amdgcn_rcpf((float)a.G);
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
@@ -1010,23 +1013,38 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             L += al[w] * g_l[w][row];
         }
     };
-    if (!fused) {
+    if constexpr (!fused) {
+        // partial records: lane (fq, fl) writes dims FD fl .. FD fl + FD - 1 of rows
+        // wave + kWaves * (4 i + fq), all its loads issued before the stores (records are
+        // 8-byte aligned: float2 stores)
         float* rec0 = a.part + P.part_off + (((uint64_t)lj * a.hkv + g) * P.splits + sp) * (uint64_t)P.rows * (2 + D) +
                       (uint64_t)r0 * (2 + D);
-        for (int row = wave; row < R; row += kWaves) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            const int row = wave + kWaves * (4 * i + fq);
+            if (row >= R) break;  // rows grow with i
             float al[kWaves], M, L;
             row_weights(row, al, M, L);
-            float* rec = rec0 + (uint64_t)row * (2 + D);
-            for (int i = lane; i < D; i += 64) {
-                float z = 0.0f;
+            float z[FD];
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) z += al[w] * g_big.accs[w * (kMaxRows * D) + row * D + i];
-                rec[2 + i] = z * inv_nu;
+            for (int e = 0; e < FD; ++e) z[e] = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float* src = g_big.accs + w * (kMaxRows * D) + row * D + FD * fl;
+#pragma unroll
+                for (int e4 = 0; e4 < FD; e4 += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(src + e4);
+                    z[e4] = fmaf(al[w], v.x, z[e4]);
+                    z[e4 + 1] = fmaf(al[w], v.y, z[e4 + 1]);
+                    z[e4 + 2] = fmaf(al[w], v.z, z[e4 + 2]);
+                    z[e4 + 3] = fmaf(al[w], v.w, z[e4 + 3]);
+                }
             }
-            if (lane == 0) {
-                rec[0] = M;
-                rec[1] = L;
-            }
+            float* rec = rec0 + (uint64_t)row * (2 + D);
+#pragma unroll
+            for (int e = 0; e < FD; e += 2)
+                *reinterpret_cast<float2*>(rec + 2 + FD * fl + e) = make_float2(z[e] * inv_nu, z[e + 1] * inv_nu);
+            if (fl == 0) *reinterpret_cast<float2*>(rec) = make_float2(M, L);
         }
         return;
     }
@@ -1115,7 +1133,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
 }
 
-template <int D, int RT, bool QSPLIT>
+template <int D, int RT, bool QSPLIT, bool FUSED>
 __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents) {
     const PoolEntry& P = a.pools[find_pool_m(a, blockIdx.x)];
     int rb = 0;
@@ -1123,22 +1141,22 @@ __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents
     local /= P.splits;
     const int l = a.l0 + local / a.hkv;
     switch (layer_bits(P, l)) {
-        case 2: pool_mfma_body<D, RT, 2, QSPLIT>(a, cents); break;
-        case 3: pool_mfma_body<D, RT, 3, QSPLIT>(a, cents); break;
-        default: pool_mfma_body<D, RT, 4, QSPLIT>(a, cents); break;
+        case 2: pool_mfma_body<D, RT, 2, QSPLIT, FUSED>(a, cents); break;
+        case 3: pool_mfma_body<D, RT, 3, QSPLIT, FUSED>(a, cents); break;
+        default: pool_mfma_body<D, RT, 4, QSPLIT, FUSED>(a, cents); break;
     }
 }
 
-template <int D, bool QSPLIT>
+template <int D, bool QSPLIT, bool FUSED>
 int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int rt) {
     switch (rt) {
-        case 1: hipLaunchKernelGGL((k_pool_mfma<D, 1, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
-        case 2: hipLaunchKernelGGL((k_pool_mfma<D, 2, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
-        case 3: hipLaunchKernelGGL((k_pool_mfma<D, 3, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c); break;
+        case 1: hipLaunchKernelGGL((k_pool_mfma<D, 1, QSPLIT, FUSED>), dim3(wg), dim3(256), 0, s, a, c); break;
+        case 2: hipLaunchKernelGGL((k_pool_mfma<D, 2, QSPLIT, FUSED>), dim3(wg), dim3(256), 0, s, a, c); break;
+        case 3: hipLaunchKernelGGL((k_pool_mfma<D, 3, QSPLIT, FUSED>), dim3(wg), dim3(256), 0, s, a, c); break;
         default:
             // split fp32 queries hold two operand sets in registers: at most 48 rows
             if constexpr (QSPLIT) return PKV_EUNSUPPORTED;
-            else hipLaunchKernelGGL((k_pool_mfma<D, 4, QSPLIT>), dim3(wg), dim3(256), 0, s, a, c);
+            else hipLaunchKernelGGL((k_pool_mfma<D, 4, QSPLIT, FUSED>), dim3(wg), dim3(256), 0, s, a, c);
             break;
     }
     return PKV_OK;
@@ -1161,8 +1179,15 @@ int launch_pool_mfma(const DecodeLaunch& a, int total_wg, hipStream_t s) {
     const int rt = (rows + 15) / 16;
     CentArg c;
     std::memcpy(c.c, codebook_tables().cent, sizeof(c.c));
-    if (a.d == 128) return split ? launch_d<128, true>(a, total_wg, s, c, rt) : launch_d<128, false>(a, total_wg, s, c, rt);
-    return split ? launch_d<64, true>(a, total_wg, s, c, rt) : launch_d<64, false>(a, total_wg, s, c, rt);
+    auto go = [&](auto d_tag, auto split_tag) {
+        constexpr int DD = decltype(d_tag)::value;
+        constexpr bool SP = decltype(split_tag)::value;
+        return a.fused ? launch_d<DD, SP, true>(a, total_wg, s, c, rt) : launch_d<DD, SP, false>(a, total_wg, s, c, rt);
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    if (a.d == 128) return split ? go(D128{}, std::true_type{}) : go(D128{}, std::false_type{});
+    return split ? go(D64{}, std::true_type{}) : go(D64{}, std::false_type{});
 }
 
 }  // namespace pkv
