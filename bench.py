@@ -138,9 +138,11 @@ def copy_calibration():
 def kernel_source_sha256():
     import hashlib
 
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_shared_kv_amd", "csrc",
-                       "pkv_decode_mfma.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_shared_kv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("pkv_decode_mfma.h", "pkv_decode_mfma.hip", "pkv_decode_mfma_split.hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def log(msg):

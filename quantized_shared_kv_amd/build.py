@@ -33,7 +33,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 OBJ_DIR = os.path.join(OUT_DIR, "obj")
 LIB = os.path.join(OUT_DIR, "libpolykv.so")
-SOURCES = ["pkv_host.cpp", "pkv_quantize.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_comix.hip",
+SOURCES = ["pkv_host.cpp", "pkv_quantize.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_decode_mfma_split.hip",
+           "pkv_comix.hip",
            "pkv_handoff.cpp", "pkv_stream.hip"]
 SAN_DIR = os.path.join(OUT_DIR, "san")
 ARCH = "gfx950"
