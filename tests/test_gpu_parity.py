@@ -300,3 +300,39 @@ def test_last_bit_conventions_on_device():
     codes = codec.unpack_codes(buf[lay.vc[0]:lay.vc[1]].reshape(4, d * 3), d, 3)
     assert np.array_equal(codes[0], np.tile(np.array([3, 3, 6, 6], np.uint8), 32))
     assert np.all(codes[1] == 5) and np.all(codes[2] == 0)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("tokens,splits", [(2080, 65), (2600, 82)])
+def test_merge_of_more_than_64_records(tokens, splits, kernel):
+    """k_merge spreads a row's split records over the 64 lanes and sums them in groups: rows with
+    more than 64 records (65 splits of a 2080-token pool, 82 of a 2600-token one: one 32-token
+    tile each; then plus the 22 splits of a 700-token private pool shared by all three agents,
+    12 rows) take several lane rounds, the private pool's records starting past the boundary."""
+    h = H()
+    print(f"[decode] merge of >64 records tokens={tokens} splits={splits} kernel={kernel}", flush=True)
+    w = wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=1, n_q_heads=4, pool_tokens=tokens, sfx_tokens=24, n_agents=3)
+    A = 3
+    dp, ref = h.build_pair(w, 0, layers=1)
+    n = 700
+    pp = h.DevicePool(1, 1, w.head_dim, n, [3])
+    pr = pool_image.PoolImage(1, 1, w.head_dim, n, [3])
+    kt, vt = w.pool_k(7, 0), w.pool_v(7, 0)
+    pr.append(0, kt.f32[None, :, :n], vt.f32[None, :, :n])
+    pp.append(0, h.stack_layers([h._slice(kt, 0, n)]), h.stack_layers([h._slice(vt, 0, n)]))
+    q, q32 = h.make_queries(w, 2, range(A))
+    sk, sv, fk, fv = h.make_suffix(w, range(A), 1)
+    lens = [24, 0, 9]
+    for prv in (None, [pp.pool] * A):
+        out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device=h.DEV)
+        wsb = pk.agent_decode_attention([dp.pool] * A, q, out, 0, sk, sv, lens, kernel=kernel, splits=splits,
+                                        private_pools=prv)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=h.DEV)
+        pk.agent_decode_attention([dp.pool] * A, q, out, 0, sk, sv, lens, workspace=ws, kernel=kernel, splits=splits,
+                                  private_pools=prv)
+        torch.cuda.synchronize()
+        want = attention.decode_call(
+            q32, [0] * A, lambda p, l, g: ref.decoded_layer(l, g), fk, fv, lens, 1,
+            private=(lambda a, l, g: pr.decoded_layer(l, g)) if prv is not None else None)
+        err = attention.max_rel_error(out.cpu().numpy().astype(np.float64), want)
+        assert err <= TOL, (prv is not None, err)
