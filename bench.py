@@ -391,11 +391,12 @@ def main():
 
 def per_layer_block(pk, w, pools, q_all, sfx_k, sfx_v, sfx_lens, steps, kernel, flush_f):
     """The decode part of the job issued the way a model's decoder issues it: per decode step,
-    32 single-layer calls (layer l's queries, suffix and outputs in their own buffers), one
-    captured HIP graph per step.  The replay of step 0's graph is checked bit for bit against
-    the same calls made eagerly, three times with eager work in between.  The pool kernel of
-    a single-layer call is timed with events on sampled calls, warm (inside the call sequence)
-    and cold (after a reduction over 1 GiB)."""
+    32 single-layer calls (layer l's queries, suffix and outputs in their own buffers), timed
+    both as one captured HIP graph per step and issued call by call; the faster gives the
+    agent-tokens/s.  The replay of step 0's graph is checked bit for bit against the same calls
+    made eagerly, three times with eager work in between.  The pool kernel of a single-layer
+    call is timed with events on sampled calls, warm (inside the call sequence) and cold (after
+    a reduction over 1 GiB)."""
     import torch
 
     dev = q_all.device
@@ -446,12 +447,15 @@ def per_layer_block(pk, w, pools, q_all, sfx_k, sfx_v, sfx_lens, steps, kernel, 
         torch.cuda.synchronize()
         job_ms.append(e0.elapsed_time(e1))
     graph_ms = float(np.median(job_ms))
-    e0.record()
-    for s in range(8):
-        step_calls(s)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_step_us = e0.elapsed_time(e1) / 8 * 1e3
+    eager_ms = []
+    for rep in range(2):  # the same decode steps issued call by call (the host stays ahead of the GPU)
+        e0.record()
+        for s in range(steps):
+            step_calls(s)
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms.append(e0.elapsed_time(e1))
+    eager_ms = min(eager_ms)
     # the pool kernel of one single-layer call
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record()
@@ -471,10 +475,14 @@ def per_layer_block(pk, w, pools, q_all, sfx_k, sfx_v, sfx_lens, steps, kernel, 
         cold.append(p0.elapsed_time(p1))
     alg = Hkv * T * (d + d * 3 // 8 + 4) + T * 4 + A * Hq * d * (2 + 4)
     cold_us, warm_us = float(np.mean(cold)) * 1e3, float(np.mean(warm)) * 1e3
-    return {"calls_per_decode_step": L, "launch": "one captured HIP graph per decode step (32 single-layer calls)",
+    best_ms = min(graph_ms, eager_ms)
+    return {"calls_per_decode_step": L,
+            "launch": ("one captured HIP graph per decode step (32 single-layer calls)" if graph_ms <= eager_ms else
+                       "32 single-layer calls per decode step issued one by one (faster here than their captured graph)"),
             "graph_replays_checked": 3,
-            "decode_agent_tokens_per_s": A * steps / (graph_ms / 1e3),
-            "decode_step_us": graph_ms / steps * 1e3, "eager_decode_step_us": eager_step_us,
+            "decode_agent_tokens_per_s": A * steps / (best_ms / 1e3),
+            "decode_step_us": best_ms / steps * 1e3, "graph_decode_step_us": graph_ms / steps * 1e3,
+            "eager_decode_step_us": eager_ms / steps * 1e3,
             "pool_kernel": {"alg_bytes_per_launch": alg, "avg_launch_us": cold_us,
                             "achieved": alg / (cold_us / 1e6) / 1e9, "frac": alg / (cold_us / 1e6) / 1e9 / HBM_PEAK_GBPS,
                             "cache": "cold: a reduction over 1 GiB before each launch", "launches": len(cold),
