@@ -1296,8 +1296,10 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
             e.rb_rows = use_mfma ? (e.rows + e.rblocks - 1) / e.rblocks : kValuRows;
             int splits = x->splits;
             // default split: enough workgroups to cover the 256 compute units (MFMA: one
-            // 4-wave workgroup per CU; VALU: two per CU)
-            const int target = use_mfma ? 256 : 512;
+            // 4-wave workgroup per CU; VALU: two per CU).  A call with few (layer, kv head) units
+            // (a single-layer call has 8) is bound by per-workgroup latency and the merge of the
+            // splits' records: 128 matrix-core workgroups measured faster than 256 there
+            const int target = use_mfma ? (units * e.rblocks < 32 ? 128 : 256) : 512;
             if (splits <= 0) splits = std::max(1, std::min(tiles, (target + units * e.rblocks - 1) / (units * e.rblocks)));
             splits = std::min(splits, tiles);
             e.chunk = (tiles + splits - 1) / splits * kTile;
