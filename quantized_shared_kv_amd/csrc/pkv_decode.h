@@ -65,6 +65,8 @@ struct DecodeLaunch {
     int32_t fused;          // the pool kernel finishes the outputs itself (one split everywhere)
     int32_t has_private;    // some agent also attends a private pool (outputs merged by k_merge)
     int32_t seg_units;      // k_seg units: (agent, layer, kv head) of the small private pools
+    int32_t sfx_wg_begin;   // >= 0: the pool kernel's workgroups from this one on do the native-window
+                            // work (4 units each) instead of a separate kernel; -1: none
     float sm_log2;          // softmax scale * log2(e)
 };
 

@@ -9,15 +9,21 @@
 // the merge kernel applies one inverse FWHT per output row.
 //
 // Launch sequence of one call (all on the caller's stream):
-//   1. k_sfx_valu    per (agent, layer, kv head): partial softmax state over
-//                    the agent's native suffix tokens (unrotated domain)
-//   2. pool kernel   per (pool, layer, kv head, token split): partial state of
-//                    all rows that read the pool (every agent of the pool times
-//                    every q head of the kv head's group), rotated domain;
-//                    k_pool_valu here or the MFMA kernel in pkv_decode_mfma.hip
-//   3. k_merge       per output row: combine splits, inverse FWHT, add suffix
+//   1. native window per (agent, layer, kv head): partial softmax state over the
+//      agent's bf16 suffix tokens (k_sfx_fast; k_sfx for fp32 operands); in a
+//      split-record matrix-core launch that leaves compute units free, extra
+//      workgroups of the pool kernel do this work beside the pool workgroups
+//   2. k_seg per (agent, layer, kv head) of a small private pool, if any
+//   3. pool kernel per (pool, layer, kv head, token split): partial state of
+//      all rows that read the pool (every agent of the pool times every q head
+//      of the kv head's group), rotated domain; the matrix-core kernel of
+//      pkv_decode_mfma.hip (k_pool_valu when asked for).  With one split per
+//      (layer, kv head) it finishes the rows itself (inverse FWHT, suffix
+//      record, normalise); otherwise
+//   4. k_merge per output row: combine splits, inverse FWHT, add the suffix
 // Softmax state is kept in log2 units: scores are scaled by sigma * log2(e).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -26,6 +32,7 @@
 
 #include "pkv_decode.h"
 #include "pkv_lanes.h"
+#include "pkv_sfx.h"
 
 namespace pkv {
 namespace {
@@ -37,8 +44,6 @@ constexpr int kThreads = 256;
 struct Centroids {
     float c[3][16];
 };
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float ld_elem(const void* p, int dtype, uint64_t i) {
     if (dtype == PKV_BF16) {
@@ -429,319 +434,6 @@ __device__ void sfx_wave(const DecodeLaunch& a, int unit, float* pbuf, uint32_t*
     }
 }
 
-// Native suffix attention for bf16 queries and a bf16 suffix, one wavefront per
-// (launch agent, layer, kv head), RS q heads per pass.  Per chunk of up to
-// kSfxChunk tokens, two sweeps over groups of 64 tokens, each group's loads all
-// issued before any is used:
-//  1. scores: LPT lanes share a token, each holding D/LPT of its dimensions and
-//     the pass's matching query slices in registers (bf16 pairs, dot2: exact
-//     products, fp32 sums); a reduce-scatter across those lanes leaves each lane
-//     RS/LPT rows, whose scores (log2 units) go to LDS;
-//  2. values: p = 2^(s - m) replaces each score in LDS, then each lane, owning 8
-//     dimensions of every 64/(D/8)-th token, accumulates p * v; a reduce-scatter
-//     across the token lanes finishes the sums.
-// The softmax reference moves only between chunks (accumulators rescaled once
-// per chunk).
-constexpr int kSfxChunk = 256;
-constexpr int kSfxGroup = 64;
-
-// Reduce-scatter step over the lane pairs that differ in bit M: on entry v[0, N)
-// are per-lane values; on exit v[0, N/2) hold the pair's sums of v[0, N/2) on the
-// lane with that bit clear and of v[N/2, N) on the other.
-template <int M, int N>
-__device__ __forceinline__ void scatter_add(float* v, bool hi) {
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-        const float send = hi ? v[i] : v[i + N / 2];
-        const float keep = hi ? v[i + N / 2] : v[i];
-        v[i] = keep + lane_xor<M>(send);
-    }
-}
-
-template <int M, int N>
-__device__ __forceinline__ void all_add(float* v) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += lane_xor<M>(v[i]);
-}
-
-// 16 bytes at base + off (base wave-uniform, off a per-lane byte offset)
-__device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
-    return *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + off);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <int D, int RS, bool PF>
-__device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
-    // score sweep: LPT lanes per token, each reading KL 16-byte chunks of it (and holding the
-    // matching query slices: RS * KL * 4 registers)
-    constexpr int LPT = (RS * D / 64) > 2 ? RS * D / 64 : 2;
-    constexpr int TPP = 64 / LPT;           // tokens per load instruction
-    constexpr int KL = D / 8 / LPT;         // 16-byte chunks per lane per token
-    constexpr int KG = TPP > (RS >= 4 ? 16 : 32) ? TPP : (RS >= 4 ? 16 : 32);  // tokens per score group
-    constexpr int KU = KG / TPP;            // load instructions per chunk index per group
-    constexpr int RPL = RS / LPT > 1 ? RS / LPT : 1;  // rows per lane after the reduction
-    constexpr int LB = LPT == 2 ? 1 : LPT == 4 ? 2 : LPT == 8 ? 3 : 4;      // log2 LPT
-    constexpr int LS = RS / RPL == 1 ? 0 : RS / RPL == 2 ? 1 : RS / RPL == 4 ? 2 : 3;  // scatter steps
-    // value sweep: LV lanes per token, 8 dimensions each
-    constexpr int LV = D / 8;
-    constexpr int TV = 64 / LV;             // tokens per load instruction
-    constexpr int VG = RS >= 4 ? 16 : 32;   // tokens per value group (bounds the probabilities held)
-    constexpr int VU = VG / TV;             // load instructions per group
-    constexpr int TB = TV == 4 ? 2 : 3;     // log2 TV
-    static_assert(KL >= 1 && LPT <= 16 && (1 << LS) * RPL == RS && (TV == 4 || TV == 8), "suffix tiling");
-
-    const int lane = threadIdx.x & 63;
-    const int g = unit % a.hkv;
-    const int lj = (unit / a.hkv) % a.lc;
-    const int k = unit / (a.hkv * a.lc);
-    const int agent = a.agent_id[k];
-    const int S = a.sfx_len[k];
-    const uint64_t tok0 = (((uint64_t)agent * a.lc + lj) * a.hkv + g) * (uint64_t)a.sfx_cap;
-    const uint16_t* K = static_cast<const uint16_t*>(a.sfx_k) + tok0 * D;
-    const uint16_t* V = static_cast<const uint16_t*>(a.sfx_v) + tok0 * D;
-
-    const int part = lane % LPT;  // score sweep: chunks part, part + LPT, ... of token lane / LPT
-    const int tl = lane / LPT;
-    int rb = 0;                   // first row this lane keeps after the reduce-scatter
-    if constexpr (LS >= 1) rb += (lane & 1) * (RS / 2);
-    if constexpr (LS >= 2) rb += ((lane >> 1) & 1) * (RS / 4);
-    if constexpr (LS >= 3) rb += ((lane >> 2) & 1) * (RS / 8);
-    // the lane bits past the scatter steps are summed over: one lane of each copy writes
-    const bool swriter = ((lane & (LPT - 1)) >> LS) == 0;
-    const int dv = lane % LV;     // value sweep: dimensions 8 dv .. 8 dv + 7 of token lane / LV
-    const int tv = lane / LV;
-
-    for (int r0 = 0; r0 < a.G; r0 += RS) {
-        const int nr = min(RS, a.G - r0);
-        float M[RS], Lp[RS], acc[RS * 8];
-#pragma unroll
-        for (int r = 0; r < RS; ++r) {
-            M[r] = -INFINITY;
-            Lp[r] = 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < RS * 8; ++i) acc[i] = 0.0f;
-
-        for (int c0 = 0; c0 < S; c0 += kSfxChunk) {
-            const int nc = min(kSfxChunk, S - c0);
-            const uint16_t* Kc = K + (uint64_t)c0 * D;
-            const uint16_t* Vc = V + (uint64_t)c0 * D;
-            // the pass's query slices, reloaded per chunk so that they are not held through the value sweep
-            uint32_t qv[RS][KL * 4];
-            uint32_t zero;
-            asm volatile("v_mov_b32 %0, 0" : "=v"(zero));  // keeps the reload inside the chunk loop
-#pragma unroll
-            for (int r = 0; r < RS; ++r) {
-                const int rr = min(r0 + r, a.G - 1);  // rows past G repeat the last one and are not stored
-                const uint16_t* qrow =
-                    static_cast<const uint16_t*>(a.q) + (((uint64_t)agent * a.lc + lj) * a.hq + g * a.G + rr) * D;
-#pragma unroll
-                for (int c = 0; c < KL; ++c) {
-                    const uint4 w = ld16(qrow, zero + (uint32_t)(c * LPT + part) * 16);
-                    qv[r][4 * c] = w.x;
-                    qv[r][4 * c + 1] = w.y;
-                    qv[r][4 * c + 2] = w.z;
-                    qv[r][4 * c + 3] = w.w;
-                }
-            }
-            // ---- 1. scores
-            float mloc[RPL];
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) mloc[i] = -INFINITY;
-            // PF: each group's K loads are issued one group ahead (the next group's while this one
-            // is scored), so a wave waits for one load latency per chunk, not one per group (for
-            // launches too small to hide the latency with other waves; it costs registers)
-            uint4 kn[KU][KL];
-            auto load_k = [&](uint4 (&dst)[KU][KL], int gs) {
-#pragma unroll
-                for (int u = 0; u < KU; ++u) {
-                    const int t = min(gs + u * TPP + tl, nc - 1);  // past the chunk: a valid token, score dropped
-                    const uint32_t off = (uint32_t)t * (D * 2) + (uint32_t)part * 16;
-#pragma unroll
-                    for (int c = 0; c < KL; ++c) dst[u][c] = ld16(Kc, off + c * LPT * 16);
-                }
-            };
-            if constexpr (PF) load_k(kn, 0);
-            for (int g0 = 0; g0 < nc; g0 += KG) {
-                uint4 kk[KU][KL];
-                if constexpr (PF) {
-#pragma unroll
-                    for (int u = 0; u < KU; ++u)
-#pragma unroll
-                        for (int c = 0; c < KL; ++c) kk[u][c] = kn[u][c];
-                    load_k(kn, g0 + KG);
-                } else {
-                    load_k(kk, g0);
-                }
-#pragma unroll
-                for (int u = 0; u < KU; ++u) {
-                    const int t = g0 + u * TPP + tl;
-                    float sc[RS];
-#pragma unroll
-                    for (int r = 0; r < RS; ++r) sc[r] = 0.0f;
-#pragma unroll
-                    for (int c = 0; c < KL; ++c) {
-                        const uint32_t kw[4] = {kk[u][c].x, kk[u][c].y, kk[u][c].z, kk[u][c].w};
-#pragma unroll
-                        for (int r = 0; r < RS; ++r)
-#pragma unroll
-                            for (int w = 0; w < 4; ++w)
-                                sc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw[w]),
-                                                                        __builtin_bit_cast(bf16x2_t, qv[r][4 * c + w]),
-                                                                        sc[r], false);
-                    }
-                    // over lane bits 0 .. LB-1: scatter the rows while more than one is left, then sum
-                    auto red = [&](auto bt) {
-                        constexpr int b = decltype(bt)::value;
-                        if constexpr (b < LS) scatter_add<(1 << b), (RS >> b)>(sc, lane & (1 << b));
-                        else if constexpr (b < LB) all_add<(1 << b), RPL>(sc);
-                    };
-                    red(std::integral_constant<int, 0>{});
-                    red(std::integral_constant<int, 1>{});
-                    red(std::integral_constant<int, 2>{});
-                    red(std::integral_constant<int, 3>{});
-                    const bool ok = t < nc;
-#pragma unroll
-                    for (int i = 0; i < RPL; ++i) {
-                        const float x = sc[i] * a.sm_log2;
-                        if (ok) {
-                            mloc[i] = fmaxf(mloc[i], x);
-                            if (swriter) sbuf[t * RS + rb + i] = x;
-                        }
-                    }
-                }
-            }
-            // chunk row maxima: over the token lanes, then each row read from a lane holding it
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-#pragma unroll
-                for (int off = LPT; off < 64; off <<= 1) mloc[i] = fmaxf(mloc[i], __shfl_xor(mloc[i], off, 64));
-            }
-#pragma unroll
-            for (int r = 0; r < RS; ++r) {
-                // rows [rb, rb + RPL) sit on the lanes whose low LS bits, reversed, give rb / RPL
-                const int q = r / RPL;
-                int src = 0;
-#pragma unroll
-                for (int b = 0; b < LS; ++b) src |= ((q >> (LS - 1 - b)) & 1) << b;
-                const float mc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mloc[r % RPL]), src));
-                const float mn = fmaxf(M[r], mc);
-                const float alpha = (M[r] == -INFINITY) ? 0.0f : exp2f(M[r] - mn);
-                M[r] = mn;
-                Lp[r] *= alpha;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r * 8 + e] *= alpha;
-            }
-            __builtin_amdgcn_wave_barrier();
-            // PF: the first value group's loads (they do not depend on the scores)
-            uint4 vn[VU];
-            auto load_v = [&](uint4 (&dst)[VU], int gs) {
-#pragma unroll
-                for (int u = 0; u < VU; ++u) {
-                    const int t = min(gs + u * TV + tv, nc - 1);  // past the chunk: a valid token, weight 0
-                    dst[u] = ld16(Vc, (uint32_t)t * (D * 2) + (uint32_t)dv * 16);
-                }
-            };
-            if constexpr (PF) load_v(vn, 0);
-            // ---- probabilities in place, per-lane partial sums
-            for (int t = lane; t < nc; t += 64) {
-#pragma unroll
-                for (int r = 0; r < RS; ++r) {
-                    const float p = exp2f(sbuf[t * RS + r] - M[r]);
-                    sbuf[t * RS + r] = p;
-                    Lp[r] += p;
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            // ---- 2. values (PF: loads one group ahead, as the keys)
-            for (int g0 = 0; g0 < nc; g0 += VG) {
-                uint4 vv[VU];
-                if constexpr (PF) {
-#pragma unroll
-                    for (int u = 0; u < VU; ++u) vv[u] = vn[u];
-                    load_v(vn, g0 + VG);
-                } else {
-                    load_v(vv, g0);
-                }
-#pragma unroll
-                for (int u = 0; u < VU; ++u) {
-                    const int t = g0 + u * TV + tv;
-                    const bool ok = t < nc;
-                    float pr[RS];
-                    if constexpr (RS >= 4) {
-#pragma unroll
-                        for (int r4 = 0; r4 < RS; r4 += 4) {
-                            const float4 p4 = *reinterpret_cast<const float4*>(&sbuf[t * RS + r4]);
-                            pr[r4] = p4.x;
-                            pr[r4 + 1] = p4.y;
-                            pr[r4 + 2] = p4.z;
-                            pr[r4 + 3] = p4.w;
-                        }
-                    } else if constexpr (RS == 2) {
-                        const float2 p2 = *reinterpret_cast<const float2*>(&sbuf[t * 2]);
-                        pr[0] = p2.x;
-                        pr[1] = p2.y;
-                    } else {
-                        pr[0] = sbuf[t];
-                    }
-#pragma unroll
-                    for (int r = 0; r < RS; ++r) pr[r] = ok ? pr[r] : 0.0f;
-                    const float v[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y),
-                                        bf16_lo(vv[u].z), bf16_hi(vv[u].z), bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
-#pragma unroll
-                    for (int r = 0; r < RS; ++r)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[r * 8 + e] = fmaf(pr[r], v[e], acc[r * 8 + e]);
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-        // ---- records: l over all lanes; acc over the token lanes, rows scattered
-#pragma unroll
-        for (int r = 0; r < RS; ++r) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) Lp[r] += __shfl_xor(Lp[r], off, 64);
-        }
-        // steps over lane bits LV, 2 LV, ...: scatter rows while more than one is left
-        constexpr int N1 = RS >= 2 ? RS / 2 : 1, N2 = RS >= 4 ? RS / 4 : 1, N3 = RS >= 8 ? RS / 8 : 1;
-        int rv = 0;          // first row this lane holds afterwards
-        bool writer = true;  // one lane per copy
-        if constexpr (RS >= 2) { scatter_add<LV, RS * 8>(acc, lane & LV); rv += ((lane >> (6 - TB)) & 1) * (RS / 2); }
-        else { all_add<LV, 8>(acc); writer = writer && !(lane & LV); }
-        if constexpr (RS >= 4) { scatter_add<2 * LV, N1 * 8>(acc, lane & (2 * LV)); rv += ((lane >> (7 - TB)) & 1) * (RS / 4); }
-        else { all_add<2 * LV, N1 * 8>(acc); writer = writer && !(lane & (2 * LV)); }
-        if constexpr (TB == 3) {
-            if constexpr (RS >= 8) { scatter_add<4 * LV, N2 * 8>(acc, lane & (4 * LV)); rv += ((lane >> 5) & 1) * (RS / 8); }
-            else { all_add<4 * LV, N2 * 8>(acc); writer = writer && !(lane & (4 * LV)); }
-        }
-        constexpr int NF = TB == 3 ? N3 : N2;  // rows per lane at the end
-        if (writer) {
-#pragma unroll
-            for (int i = 0; i < NF; ++i) {
-                const int r = rv + i;
-                if (r < nr) {
-                    float* rec = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + g * a.G + r0 + r) * (2 + D);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) rec[2 + 8 * dv + e] = acc[i * 8 + e];
-                }
-            }
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < RS; ++r) {
-                if (r < nr) {
-                    float* rec = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + g * a.G + r0 + r) * (2 + D);
-                    rec[0] = M[r];
-                    rec[1] = Lp[r];
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
 // grid ceil(n_agents * lc * hkv / 4), 256 threads = 4 wavefronts, one unit each
 template <int D, int RS, bool PF>
 __global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
@@ -1066,14 +758,15 @@ __global__ void __launch_bounds__(256) k_sfx(DecodeLaunch a) {
 
 // One wavefront per output row (launch agent, layer, q head): combine the
 // pool's split records, apply the inverse FWHT (H / d) to the rotated-domain
-// accumulator, fold in the suffix record and normalise.  The records' (m, l)
-// are spread over the lanes (record j on lane j % 64), so their loads are all in
-// flight at once; the accumulators are then summed eight records at a time,
-// their loads issued before any is used.
+// accumulator, fold in the suffix record and normalise.  Every load whose address
+// is known up front is issued first, so the row costs about one memory round trip:
+// the suffix record, the records' (m, l) spread over the lanes (record j on lane
+// j % 64) and the accumulators of the first U records; further records (more than U
+// splits) are summed U at a time, their loads issued before any is used.
 template <int D>
 __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     constexpr int EPL = D / 64;
-    constexpr int U = 8;  // records whose accumulator loads are in flight together
+    constexpr int U = 16;  // records whose accumulator loads are in flight together
     const int lane = threadIdx.x & 63;
     const uint64_t row = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const uint64_t n_rows = (uint64_t)a.n_agents * a.lc * a.hq;
@@ -1082,6 +775,17 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     const int lj = (row / a.hq) % a.lc;
     const int k = row / ((uint64_t)a.hq * a.lc);
     const int g = h / a.G;
+    // the suffix record of the row
+    float su_m = -INFINITY, su_l = 0.0f, su_v[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) su_v[e] = 0.0f;
+    if (a.has_sfx) {
+        const float* ru = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + h) * (2 + D);
+        su_m = ru[0];
+        su_l = ru[1];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) su_v[e] = ru[2 + EPL * lane + e];
+    }
     // the agent's pool and, if it has one, its private pool: split records of both, all in
     // the rotated domain, merged before the one inverse transform (records 0 .. n0-1 the pool's)
     auto records = [&](int which, const float*& rec0, uint64_t& stride, int& splits) {
@@ -1099,9 +803,23 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     if (a.agent_pool2[k] >= 0) records(1, base1, st1, n1);
     const int nrec = n0 + n1;
     auto rec = [&](int j) { return j < n0 ? base0 + (uint64_t)j * st0 : base1 + (uint64_t)(j - n0) * st1; };
+    // this lane's record of the first 64 (m, l) and the first U records' accumulators
+    float m0 = -INFINITY, l0 = 0.0f;
+    if (lane < nrec) {
+        const float* r = rec(lane);
+        m0 = r[0];
+        l0 = r[1];
+    }
+    float v[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float* r = rec(min(u, nrec - 1)) + 2 + EPL * lane;  // past the end: a valid record, weight 0
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[u][e] = r[e];
+    }
     // M = max of the records' m; L = sum of 2^(m - M) l
-    float M = -INFINITY;
-    for (int j = lane; j < nrec; j += 64) M = fmaxf(M, rec(j)[0]);
+    float M = m0;
+    for (int j = lane + 64; j < nrec; j += 64) M = fmaxf(M, rec(j)[0]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     float L = 0.0f, z[EPL];
@@ -1112,20 +830,24 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
             // this lane's record c + lane: its weight (0 past the end and for empty records)
             float wt = 0.0f;
             if (c + lane < nrec) {
-                const float* r = rec(c + lane);
-                const float m = r[0];
+                float m = m0, lv = l0;
+                if (c > 0) {
+                    const float* r = rec(c + lane);
+                    m = r[0];
+                    lv = r[1];
+                }
                 wt = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-                L += wt * r[1];
+                L += wt * lv;
             }
             const int nc = min(64, nrec - c);
             for (int j0 = 0; j0 < nc; j0 += U) {
-                float v[U][EPL];
+                if (c > 0 || j0 > 0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int j = c + min(j0 + u, nc - 1);  // past the end: a valid record, weight 0
-                    const float* r = rec(j) + 2 + EPL * lane;
+                    for (int u = 0; u < U; ++u) {
+                        const float* r = rec(c + min(j0 + u, nc - 1)) + 2 + EPL * lane;
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) v[u][e] = r[e];
+                        for (int e = 0; e < EPL; ++e) v[u][e] = r[e];
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -1164,14 +886,12 @@ __global__ void __launch_bounds__(kThreads) k_merge(DecodeLaunch a) {
     float o[EPL];
     float denom;
     if (a.has_sfx) {
-        const float* ru = a.part + a.sfx_part_off + (((uint64_t)k * a.lc + lj) * a.hq + h) * (2 + D);
-        const float mu = ru[0];
-        const float M2 = fmaxf(M, mu);
+        const float M2 = fmaxf(M, su_m);
         const float ap = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
-        const float au = (mu == -INFINITY) ? 0.0f : exp2f(mu - M2);
-        denom = ap * L + au * ru[1];
+        const float au = (su_m == -INFINITY) ? 0.0f : exp2f(su_m - M2);
+        denom = ap * L + au * su_l;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = ap * z[e] * inv_d + au * ru[2 + EPL * lane + e];
+        for (int e = 0; e < EPL; ++e) o[e] = ap * z[e] * inv_d + au * su_v[e];
     } else {
         denom = L;
 #pragma unroll
@@ -1250,6 +970,7 @@ int make_plan(const pkv_decode_args* x, bool use_mfma, Plan* plan) {
     while (ci < chunks.size()) {
         DecodeLaunch L;
         std::memset(&L, 0, sizeof(L));
+        L.sfx_wg_begin = -1;
         L.q = x->q;
         L.sfx_k = x->sfx_k;
         L.sfx_v = x->sfx_v;
@@ -1447,6 +1168,20 @@ int validate(const pkv_decode_args* x) {
     return PKV_OK;
 }
 
+// Compute units of the current device (cached per device; 0 if the query fails, which keeps
+// every launch on its own kernel)
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D, bool PF>
 void launch_sfx_fast(const DecodeLaunch& L, dim3 grid, hipStream_t s) {
     if (L.G == 1) hipLaunchKernelGGL((k_sfx_fast<D, 1, PF>), grid, dim3(kThreads), 0, s, L);
@@ -1462,10 +1197,17 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
     for (size_t i = 0; i < plan.launches.size(); ++i) {
         DecodeLaunch L = plan.launches[i];
         L.part = ws;
+        int pool_wg = plan.pool_wg[i];
         if (L.has_sfx) {
             const int units = L.n_agents * L.lc * L.hkv;
             const dim3 grid((units + 3) / 4);
-            if (L.q_dtype == PKV_BF16 && L.sfx_dtype == PKV_BF16) {
+            // a split-record matrix-core launch that leaves compute units free takes the window's
+            // workgroups itself: both run side by side, one launch fewer (k_merge joins them)
+            const bool bf16 = L.q_dtype == PKV_BF16 && L.sfx_dtype == PKV_BF16;
+            if (use_mfma && !L.fused && bf16 && pool_wg + (int)grid.x <= cu_count()) {
+                L.sfx_wg_begin = pool_wg;
+                pool_wg += (int)grid.x;
+            } else if (bf16) {
                 // rows per pass: the group size rounded up to a power of two, at most 8; with fewer
                 // waves than SIMDs (e.g. a single-layer call) latency rules, so each wave keeps its
                 // next load group in flight; with more, other waves hide it at the lower register count
@@ -1487,7 +1229,7 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
         if (use_mfma) {
             // L.fused (set by the plan): one split per (pool, layer, kv head) and every private pool
             // a segment, so the MFMA kernel finishes the rows itself
-            const int st = launch_pool_mfma(L, plan.pool_wg[i], s);
+            const int st = launch_pool_mfma(L, pool_wg, s);
             if (st != PKV_OK) return st;
         } else {
             hipLaunchKernelGGL(k_pool_valu<D>, dim3(plan.pool_wg[i]), dim3(kThreads), 0, s, L, cents);

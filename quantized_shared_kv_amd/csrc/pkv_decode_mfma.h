@@ -56,6 +56,7 @@
 
 #include "pkv_decode.h"
 #include "pkv_lanes.h"
+#include "pkv_sfx.h"
 
 namespace pkv {
 namespace {
@@ -1138,8 +1139,30 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
 }
 
+// The native-window work a split-record launch carries beside the pool (workgroups from
+// a.sfx_wg_begin on): 4 (agent, layer, kv head) units per workgroup, as the suffix kernel, with
+// this launch's LDS (unused by such a workgroup otherwise) as each wave's score buffer.
+template <int D>
+__device__ __forceinline__ void pool_launch_sfx(const DecodeLaunch& a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = ((int)blockIdx.x - a.sfx_wg_begin) * 4 + wave;
+    if (unit >= a.n_agents * a.lc * a.hkv) return;
+    float* sbuf = big_lds<D>().accs + wave * (kSfxChunk * 8);
+    if (a.G == 1) sfx_fast_wave<D, 1, true>(a, unit, sbuf);
+    else if (a.G == 2) sfx_fast_wave<D, 2, true>(a, unit, sbuf);
+    else if (a.G <= 4) sfx_fast_wave<D, 4, true>(a, unit, sbuf);
+    else sfx_fast_wave<D, 8, true>(a, unit, sbuf);
+}
+static_assert(kWaves * kSfxChunk * 8 <= kWaves * kMaxRows * 64, "window score buffers fit the LDS");
+
 template <int D, int RT, bool QSPLIT, bool FUSED>
 __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents) {
+    if constexpr (!FUSED) {
+        if (a.sfx_wg_begin >= 0 && (int)blockIdx.x >= a.sfx_wg_begin) {
+            pool_launch_sfx<D>(a);
+            return;
+        }
+    }
     const PoolEntry& P = a.pools[find_pool_m(a, blockIdx.x)];
     int rb = 0;
     int local = pool_item_of_wg(blockIdx.x - P.wg_begin, a.lc * a.hkv * P.splits, P.rblocks, &rb);
