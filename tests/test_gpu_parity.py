@@ -336,3 +336,26 @@ def test_merge_of_more_than_64_records(tokens, splits, kernel):
             private=(lambda a, l, g: pr.decoded_layer(l, g)) if prv is not None else None)
         err = attention.max_rel_error(out.cpu().numpy().astype(np.float64), want)
         assert err <= TOL, (prv is not None, err)
+
+
+def test_single_layer_calls_match_the_all_layer_call():
+    """The same decode step as one all-layer call (one split per (layer, kv head), the pool kernel
+    finishing the rows after the separate native-window kernel) and as single-layer calls (token
+    splits, the window's workgroups inside the pool launch, k_merge): outputs agree to summation
+    order, and both match the oracle."""
+    print("[decode] single-layer calls vs all-layer call", flush=True)
+    h = H()
+    w = wl.LLAMA3_8B.replace(n_layers=2, pool_tokens=700, sfx_tokens=40, n_agents=15)
+    A, L, Hq = w.n_agents, w.n_layers, w.n_q_heads
+    dp, ref = h.build_pair(w, 0)
+    q, q32 = h.make_queries(w, 0, range(A))
+    kd, vd, ksf, vsf = h.make_suffix(w, range(A), L)
+    lens = [(7 * a) % 41 for a in range(A)]
+    whole = h.run_decode([dp.pool] * A, q, (kd, vd), lens, splits=1)  # the fused form
+    per = np.concatenate([h.run_decode([dp.pool] * A, q[:, l:l + 1].contiguous(),
+                                       (kd[:, l:l + 1].contiguous(), vd[:, l:l + 1].contiguous()), lens, layer_begin=l)
+                          for l in range(L)], axis=1)
+    assert attention.max_rel_error(per, whole) <= 1e-5
+    want = h.oracle_decode(q32, [0] * A, [ref], ksf, vsf, lens, w.n_kv_heads)
+    assert attention.max_rel_error(whole, want) <= TOL
+    assert attention.max_rel_error(per, want) <= TOL
