@@ -913,19 +913,23 @@ def comix_bench():
             "attention_rel_error_worst_item": {"uniform_3bit": float(e_uni.max()), "allocated": float(e_alloc.max())},
         }
         log(f"[comix] {recipe}: {json.dumps(res[recipe])}")
-    # sensitivity kernel roofline: fp32 multiply-adds of the scores and the ||v|| sums
+    # sensitivity kernel roofline: with bf16 operands the scores run on the matrix cores and the
+    # kernel streams the windows (bf16 K and V) and the recent queries once: bound by HBM; the
+    # multiply-adds (scores and ||v|| sums) are reported beside it
     flops = A * L * Hkv * (R * (Hq // Hkv) * S * d * 2 + S * d * 2)
+    sens_bytes = A * L * Hkv * S * d * 2 * 2 + R * A * L * Hq * d * 2 + A * L * 4
     first = res["channel_lognormal"]
+    sens_s = first["sensitivity_us"] * 1e-6
     print(json.dumps({"metric": "CoMixKV controller: sensitivity kernel time and allocation quality",
                       "value": first["sensitivity_us"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
-                      "dtype": "f32", "data": "synthetic",
+                      "dtype": "bf16 operands, fp32 accumulation", "data": "synthetic",
                       "config": {"workload": "qwen3_32b_comix_controller", "agents": A, "layers": L, "q_heads": Hq,
                                  "kv_heads": Hkv, "head_dim": d, "window": S, "recent_steps": R,
                                  "budget": "bytes of 3 bits everywhere"},
-                      "roofline": {"bound": "alu", "achieved": flops / (first["sensitivity_us"] * 1e-6) / 1e12,
-                                   "peak": 157.3, "unit": "TFLOP/s",
-                                   "frac": flops / (first["sensitivity_us"] * 1e-6) / 1e12 / 157.3,
-                                   "kernel": "comix sensitivity", "flops_per_launch": flops},
+                      "roofline": {"bound": "hbm", "achieved": sens_bytes / sens_s / 1e9, "peak": HBM_PEAK_GBPS,
+                                   "unit": "GB/s", "frac": sens_bytes / sens_s / 1e9 / HBM_PEAK_GBPS,
+                                   "kernel": "comix sensitivity (k_comix_mfma)", "bytes_per_launch": sens_bytes,
+                                   "flops_per_launch": flops, "tflops": flops / sens_s / 1e12},
                       "recipes": res}), flush=True)
 
 

@@ -15,7 +15,8 @@
 // The sensitivity of (agent, layer) is sum_t p_t ||v_t|| averaged over the
 // agent's recent query rows (steps x query heads).
 //
-// k_comix_sens: one workgroup of 4 wavefronts per (agent, layer); wavefront w
+// k_comix_sens (fp32 operands; bf16 ones take k_comix_mfma, below): one workgroup
+// of 4 wavefronts per (agent, layer); wavefront w
 // takes kv heads w, w + 4, ...; for each, up to 32 query rows at a time are
 // staged in LDS (fp32) and the window is swept 32 tokens at a time, two lanes
 // per token: lane half h holds the 16-byte chunks 2i + h of its token's key row
@@ -206,6 +207,146 @@ __global__ void __launch_bounds__(256) k_comix_sens(ComixLaunch a) {
         a.out[(uint64_t)k * a.lc + lj] = n > 0 ? ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) * a.inv_rows : 0.0f;
 }
 
+// k_comix_mfma: the same sums for bf16 queries and a bf16 window, with the scores on the matrix
+// cores (v_mfma_f32_16x16x32_bf16: bf16 products are exact in fp32 and summed in fp32, as the
+// vector kernel's fma chain does, in another order).  One workgroup per (agent, layer);
+// wavefront w takes kv heads w, w + 4, ...; per kv head up to 64 query rows (4 tiles of 16) at a
+// time are held as A operands, and the window is swept 16 tokens at a time: lane (kg, c) loads
+// the B operands of token c of the tile (dimensions 32 s + 8 kg .. + 7 of every k-step s) and a
+// quarter of its value row for ||v||, the next tile's loads in flight while the current one is
+// used.  The lane keeps an online (max, sum p, sum p ||v||) of rows 4 kg + j of each tile over
+// its tokens; the 16 token lanes' states are merged at the end and the rows summed in a fixed
+// order, so the result is deterministic.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ void __launch_bounds__(256) k_comix_mfma(ComixLaunch a) {
+    constexpr int KS = D / 32;  // k-steps of the scores
+    constexpr int RTM = 4;      // row tiles of 16 per pass over the window
+    constexpr int VQ = D / 4;   // value dimensions per lane (a quarter of the row)
+    __shared__ float wsum[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kl = blockIdx.x / a.lc;  // agent within the launch
+    const int lj = blockIdx.x % a.lc;
+    const int k = a.agent0 + kl;
+    const int n = a.len[kl];
+    const int NR = a.n_recent * a.G;
+    const int c = lane & 15, kg = lane >> 4;
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
+
+    float total = 0.0f;  // this wavefront's sum of row values, fixed order
+    if (n > 0) {
+        for (int g = wave; g < a.hkv; g += 4) {
+            const uint64_t wrow = (((uint64_t)k * a.lc + lj) * a.hkv + g) * (uint64_t)a.cap;
+            const uint16_t* wk = static_cast<const uint16_t*>(a.win_k) + wrow * D;
+            const uint16_t* wv = static_cast<const uint16_t*>(a.win_v) + wrow * D;
+            for (int r0 = 0; r0 < NR; r0 += 16 * RTM) {
+                // A operands: row r0 + 16 rt + c (step row / G, q head g G + row % G)
+                bf16x8_t qa[RTM][KS];
+#pragma unroll
+                for (int rt = 0; rt < RTM; ++rt) {
+                    const int row = r0 + 16 * rt + c;
+                    const int rs = row / a.G, h = g * a.G + row % a.G;
+                    const uint64_t qo = ((((uint64_t)rs * a.n_agents_total + k) * a.lc + lj) * a.hq + h) * D + 8 * kg;
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const uint4 v = row < NR ? *reinterpret_cast<const uint4*>(q16 + qo + 32 * s) : make_uint4(0, 0, 0, 0);
+                        qa[rt][s] = __builtin_bit_cast(bf16x8_t, v);
+                    }
+                }
+                float m[RTM][4], l[RTM][4], u[RTM][4];
+#pragma unroll
+                for (int rt = 0; rt < RTM; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        m[rt][j] = -INFINITY;
+                        l[rt][j] = 0.0f;
+                        u[rt][j] = 0.0f;
+                    }
+                auto load_tile = [&](int t0, uint4 (&kb)[KS], uint4 (&vb)[VQ / 8]) {
+                    const uint64_t t = (uint64_t)min(t0 + c, n - 1);  // past the window: a valid row, unused
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) kb[s] = *reinterpret_cast<const uint4*>(wk + t * D + 32 * s + 8 * kg);
+#pragma unroll
+                    for (int i = 0; i < VQ / 8; ++i) vb[i] = *reinterpret_cast<const uint4*>(wv + t * D + VQ * kg + 8 * i);
+                };
+                uint4 kb[KS], vb[VQ / 8];
+                load_tile(0, kb, vb);
+                for (int t0 = 0; t0 < n; t0 += 16) {
+                    uint4 kn[KS], vnx[VQ / 8];
+                    const bool more = t0 + 16 < n;
+                    if (more) load_tile(t0 + 16, kn, vnx);
+                    // ||v|| of token t0 + c: this lane's quarter of the row, then the four quarters
+                    float vv = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < VQ / 8; ++i) {
+                        const uint32_t w4[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xffff0000u);
+                            vv = fmaf(lo, lo, vv);
+                            vv = fmaf(hi, hi, vv);
+                        }
+                    }
+                    vv += lane_xor<16>(vv);
+                    vv += lane_xor<32>(vv);
+                    const float vn = sqrtf(vv);
+                    const bool ok = t0 + c < n;
+#pragma unroll
+                    for (int rt = 0; rt < RTM; ++rt) {
+                        if (r0 + 16 * rt >= NR) break;  // wave-uniform
+                        f32x4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int s = 0; s < KS; ++s)
+                            S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], __builtin_bit_cast(bf16x8_t, kb[s]), S, 0, 0, 0);
+                        if (ok) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float sc = S[j] * a.sm_log2;
+                                const float mn = fmaxf(m[rt][j], sc);
+                                const float al = exp2f(m[rt][j] - mn), e = exp2f(sc - mn);
+                                l[rt][j] = l[rt][j] * al + e;
+                                u[rt][j] = u[rt][j] * al + e * vn;
+                                m[rt][j] = mn;
+                            }
+                        }
+                    }
+                    if (more) {
+#pragma unroll
+                        for (int s = 0; s < KS; ++s) kb[s] = kn[s];
+#pragma unroll
+                        for (int i = 0; i < VQ / 8; ++i) vb[i] = vnx[i];
+                    }
+                }
+                // merge the 16 token lanes' states of each row, then sum this lane group's rows
+                // (4 kg + j of each tile) in order and the four groups in a fixed tree
+                float part = 0.0f;
+#pragma unroll
+                for (int rt = 0; rt < RTM; ++rt) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        merge_lanes<1>(m[rt][j], l[rt][j], u[rt][j]);
+                        merge_lanes<2>(m[rt][j], l[rt][j], u[rt][j]);
+                        merge_lanes<4>(m[rt][j], l[rt][j], u[rt][j]);
+                        merge_lanes<8>(m[rt][j], l[rt][j], u[rt][j]);
+                        const int row = r0 + 16 * rt + 4 * kg + j;
+                        if (row < NR) part += l[rt][j] > 0.0f ? u[rt][j] / l[rt][j] : 0.0f;
+                    }
+                }
+                part += lane_xor<16>(part);
+                part += lane_xor<32>(part);
+                total += part;
+            }
+        }
+    }
+    if (lane == 0) wsum[wave] = total;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        a.out[(uint64_t)k * a.lc + lj] = n > 0 ? ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) * a.inv_rows : 0.0f;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -258,8 +399,15 @@ int comix_sensitivity(const pkv_comix_args* x, void* stream) {
         L.n_agents = std::min(kComixAgents, x->n_agents - a0);
         for (int i = 0; i < L.n_agents; ++i) L.len[i] = x->win_len[a0 + i];
         const dim3 grid((unsigned)(L.n_agents * L.lc));
-        if (x->head_dim == 128) hipLaunchKernelGGL(k_comix_sens<128>, grid, dim3(256), 0, s, L);
-        else hipLaunchKernelGGL(k_comix_sens<64>, grid, dim3(256), 0, s, L);
+        // bf16 operands: scores on the matrix cores; fp32 ones: the vector kernel
+        const bool mfma = L.q_bf16 && L.win_bf16;
+        if (x->head_dim == 128) {
+            if (mfma) hipLaunchKernelGGL(k_comix_mfma<128>, grid, dim3(256), 0, s, L);
+            else hipLaunchKernelGGL(k_comix_sens<128>, grid, dim3(256), 0, s, L);
+        } else {
+            if (mfma) hipLaunchKernelGGL(k_comix_mfma<64>, grid, dim3(256), 0, s, L);
+            else hipLaunchKernelGGL(k_comix_sens<64>, grid, dim3(256), 0, s, L);
+        }
     }
     return launch_status();
 }

@@ -1,9 +1,10 @@
 """GPU parity of the CoMixKV sensitivity kernel and the controller end to end.
 
 comix_sensitivity (one workgroup per (agent, layer), fp32 online softmax over
-the native window) against the oracle's fp64 definition: small ragged cases
+the native window; bf16 operands take the matrix-core kernel, fp32 ones the
+vector kernel) against the oracle's fp64 definition: small ragged cases
 (empty, one-token and odd windows, GQA 4 and 8, MHA d 64, fp32 and bf16, more
-than 32 query rows per kv head), and sampled entries at the Qwen3-32B shape
+than 32 and more than 64 query rows per kv head), and sampled entries at the Qwen3-32B shape
 (8 agents, 64 layers, 64/8 heads, 128-token windows, 8 recent steps).  Then
 the allocation on the device-measured sensitivities equals the oracle's
 allocation on the oracle's sensitivities whenever their greedy choices are not
@@ -51,6 +52,10 @@ CASES = {
     "g8_40_rows": (wl.QWEN3_32B_MIXED.replace(n_layers=2, n_agents=2, sfx_tokens=50), 5, [50, 13], "bf16"),
     "g8_d64_bf16": (wl.SMOLLM2.replace(n_layers=3, n_q_heads=16, n_kv_heads=2, n_agents=2, sfx_tokens=9),
                     1, [9, 4], "bf16"),
+    # 9 steps x 8 heads = 72 rows per kv head: the matrix-core kernel's second pass over the window
+    "g8_72_rows_bf16": (wl.QWEN3_32B_MIXED.replace(n_layers=2, n_agents=2, sfx_tokens=37), 9, [37, 20], "bf16"),
+    "g4_72_rows_f32": (wl.LLAMA3_8B.replace(n_layers=1, n_kv_heads=2, n_q_heads=8, n_agents=2, sfx_tokens=33),
+                       18, [33, 1], "f32"),
 }
 
 
