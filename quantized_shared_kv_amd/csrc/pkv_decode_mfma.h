@@ -123,6 +123,31 @@ __device__ __forceinline__ int find_pool_m(const DecodeLaunch& a, int wg) {
     return p;
 }
 
+// The set-up reads the kernel arguments as a chain (the pool's index, then its entry, then
+// the rows' fields), and each first touch of a 64-byte argument line waits for memory.  One
+// scalar load per line of the launch's scalar fields, pool entry 0 and the centroid table,
+// waited for together, puts those lines in the scalar cache (and the L2) first.  The loads
+// address the kernel-argument segment directly (DecodeLaunch at offset 0, CentArg after it):
+// taking the address of a by-value argument would make the compiler copy it to scratch.
+__device__ __forceinline__ void touch_kernel_args() {
+    constexpr int kPool = sizeof(PoolEntry) - 4;            // last word of pool entry 0
+    constexpr int kS0 = offsetof(DecodeLaunch, q);          // first scalar field
+    constexpr int kS1 = offsetof(DecodeLaunch, sm_log2);    // last scalar field
+    constexpr int kC0 = (sizeof(DecodeLaunch) + alignof(CentArg) - 1) / alignof(CentArg) * alignof(CentArg);
+    constexpr int kC1 = kC0 + sizeof(CentArg) - 4;          // last word of the centroid table
+    static_assert(kPool > 128 && kPool < 192 && kS1 - kS0 > 64 && kS1 - kS0 <= 128 && kC1 - kC0 > 128 &&
+                      kC1 - kC0 < 192,
+                  "the argument lines touched");
+    const __attribute__((address_space(4))) uint32_t* k =
+        (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+    constexpr int offs[11] = {0, 64, 128, kPool, kS0, kS0 + 64, kS1, kC0, kC0 + 64, kC0 + 128, kC1};
+    uint32_t x[11];
+#pragma unroll
+    for (int i = 0; i < 11; ++i) x[i] = k[offs[i] / 4];
+    asm volatile("" ::"s"(x[0]), "s"(x[1]), "s"(x[2]), "s"(x[3]), "s"(x[4]), "s"(x[5]), "s"(x[6]), "s"(x[7]),
+                 "s"(x[8]), "s"(x[9]), "s"(x[10]));
+}
+
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     const half2v v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
@@ -945,41 +970,61 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     float se_m[FI], se_l[FI], se_v[FI][FD];  // the agent's private segment record (rotated domain), if any
     int f_row[FI], f_head[FI], f_agent[FI];
     if constexpr (fused) {
+        // Every row's indices first, then each kind of load for all rows at once under one
+        // wave-uniform branch: a per-row branch around a lookup would make each row wait for
+        // the loads of the rows before it.
         const float rG = __builtin_amdgcn_rcpf((float)a.G);
+        int f_ka[FI];  // the row's agent among the pool's agents
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
             const int row = min(wave + kWaves * (4 * i + fq), R - 1);  // rows past R: computed, not stored
             const int prow = r0 + row;                                  // pool row
             const int ka = (int)(((float)prow + 0.5f) * rG);  // prow / G, exact for rows < 2^20
             f_row[i] = row;
+            f_ka[i] = ka;
             f_head[i] = g * a.G + prow - ka * a.G;
-            f_agent[i] = P.agent_base >= 0 ? P.agent_base + ka : a.agent_id[P.agent0 + ka];
             su_m[i] = -INFINITY;
             su_l[i] = 0.0f;
+            se_m[i] = -INFINITY;
+            se_l[i] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < FD; ++e) su_v[i][e] = 0.0f;
-            if (a.has_sfx) {
-                const float* ru =
-                    a.part + a.sfx_part_off + (((uint64_t)(P.agent0 + ka) * a.lc + lj) * a.hq + f_head[i]) * (2 + D);
+            for (int e = 0; e < FD; ++e) {
+                su_v[i][e] = 0.0f;
+                se_v[i][e] = 0.0f;
+            }
+        }
+        if (P.agent_base >= 0) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i) f_agent[i] = P.agent_base + f_ka[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < FI; ++i) f_agent[i] = a.agent_id[P.agent0 + f_ka[i]];
+        }
+        if (a.has_sfx) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i) {
+                const float* ru = a.part + a.sfx_part_off +
+                                  (((uint64_t)(P.agent0 + f_ka[i]) * a.lc + lj) * a.hq + f_head[i]) * (2 + D);
                 su_m[i] = ru[0];
                 su_l[i] = ru[1];
 #pragma unroll
                 for (int e = 0; e < FD; ++e) su_v[i][e] = ru[2 + FD * fl + e];
             }
-            se_m[i] = -INFINITY;
-            se_l[i] = 0.0f;
+        }
+        if (a.has_private) {
 #pragma unroll
-            for (int e = 0; e < FD; ++e) se_v[i][e] = 0.0f;
-            const int e2 = a.has_private ? a.agent_pool2[P.agent0 + ka] : -1;
-            if (e2 >= 0) {  // written by the segment kernel before this launch
-                const PoolEntry& Q = a.pools[e2];
-                const float* rs = a.part + Q.part_off +
-                                  (((uint64_t)lj * a.hkv + g) * Q.rows + a.agent_pos2[P.agent0 + ka] * a.G +
-                                   (f_head[i] - g * a.G)) * (2 + D);
-                se_m[i] = rs[0];
-                se_l[i] = rs[1];
+            for (int i = 0; i < FI; ++i) {
+                const int e2 = a.agent_pool2[P.agent0 + f_ka[i]];
+                if (e2 >= 0) {  // written by the segment kernel before this launch
+                    const PoolEntry& Q = a.pools[e2];
+                    const float* rs = a.part + Q.part_off +
+                                      (((uint64_t)lj * a.hkv + g) * Q.rows + a.agent_pos2[P.agent0 + f_ka[i]] * a.G +
+                                       (f_head[i] - g * a.G)) * (2 + D);
+                    se_m[i] = rs[0];
+                    se_l[i] = rs[1];
 #pragma unroll
-                for (int e = 0; e < FD; ++e) se_v[i][e] = rs[2 + FD * fl + e];
+                    for (int e = 0; e < FD; ++e) se_v[i][e] = rs[2 + FD * fl + e];
+                }
             }
         }
     }
@@ -1157,6 +1202,7 @@ static_assert(kWaves * kSfxChunk * 8 <= kWaves * kMaxRows * 64, "window score bu
 
 template <int D, int RT, bool QSPLIT, bool FUSED>
 __global__ void __launch_bounds__(256) k_pool_mfma(DecodeLaunch a, CentArg cents) {
+    touch_kernel_args();
     if constexpr (!FUSED) {
         if (a.sfx_wg_begin >= 0 && (int)blockIdx.x >= a.sfx_wg_begin) {
             pool_launch_sfx<D>(a);
