@@ -434,14 +434,15 @@ __device__ void sfx_wave(const DecodeLaunch& a, int unit, float* pbuf, uint32_t*
     }
 }
 
-// grid ceil(n_agents * lc * hkv / 4), 256 threads = 4 wavefronts, one unit each
+// grid n_agents * lc * hkv: one single-wavefront workgroup per unit.  Workgroups of one
+// wavefront spread the units evenly over the compute units (four-wavefront workgroups put
+// 16 units on some and 12 on others at 3840 units, and the fuller ones set the time).
 template <int D, int RS, bool PF>
-__global__ void __launch_bounds__(256) k_sfx_fast(DecodeLaunch a) {
-    __shared__ __align__(16) float sbuf[4][kSfxChunk * RS];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = blockIdx.x * 4 + wave;
+__global__ void __launch_bounds__(64) k_sfx_fast(DecodeLaunch a) {
+    __shared__ __align__(16) float sbuf[kSfxChunk * RS];
+    const int unit = blockIdx.x;
     if (unit >= a.n_agents * a.lc * a.hkv) return;
-    sfx_fast_wave<D, RS, PF>(a, unit, sbuf[wave]);
+    sfx_fast_wave<D, RS, PF>(a, unit, sbuf);
 }
 
 // ------------------------------------------------------------------ private segments
@@ -1183,11 +1184,12 @@ int cu_count() {
 }
 
 template <int D, bool PF>
-void launch_sfx_fast(const DecodeLaunch& L, dim3 grid, hipStream_t s) {
-    if (L.G == 1) hipLaunchKernelGGL((k_sfx_fast<D, 1, PF>), grid, dim3(kThreads), 0, s, L);
-    else if (L.G == 2) hipLaunchKernelGGL((k_sfx_fast<D, 2, PF>), grid, dim3(kThreads), 0, s, L);
-    else if (L.G <= 4) hipLaunchKernelGGL((k_sfx_fast<D, 4, PF>), grid, dim3(kThreads), 0, s, L);
-    else hipLaunchKernelGGL((k_sfx_fast<D, 8, PF>), grid, dim3(kThreads), 0, s, L);
+void launch_sfx_fast(const DecodeLaunch& L, int units, hipStream_t s) {
+    const dim3 grid(units), block(64);
+    if (L.G == 1) hipLaunchKernelGGL((k_sfx_fast<D, 1, PF>), grid, block, 0, s, L);
+    else if (L.G == 2) hipLaunchKernelGGL((k_sfx_fast<D, 2, PF>), grid, block, 0, s, L);
+    else if (L.G <= 4) hipLaunchKernelGGL((k_sfx_fast<D, 4, PF>), grid, block, 0, s, L);
+    else hipLaunchKernelGGL((k_sfx_fast<D, 8, PF>), grid, block, 0, s, L);
 }
 
 template <int D>
@@ -1211,8 +1213,8 @@ int enqueue(const Plan& plan, bool use_mfma, float* ws, void* const* events, hip
                 // rows per pass: the group size rounded up to a power of two, at most 8; with fewer
                 // waves than SIMDs (e.g. a single-layer call) latency rules, so each wave keeps its
                 // next load group in flight; with more, other waves hide it at the lower register count
-                if (units < 1024) launch_sfx_fast<D, true>(L, grid, s);
-                else launch_sfx_fast<D, false>(L, grid, s);
+                if (units < 1024) launch_sfx_fast<D, true>(L, units, s);
+                else launch_sfx_fast<D, false>(L, units, s);
             } else {
                 hipLaunchKernelGGL(k_sfx<D>, grid, dim3(kThreads), 0, s, L);
             }
