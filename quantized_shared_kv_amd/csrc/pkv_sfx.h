@@ -52,6 +52,16 @@ __device__ __forceinline__ uint4 ld16(const void* base, uint32_t off) {
     return *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + off);
 }
 
+// The same for the window's keys and values, which a call reads once: a non-temporal load, so
+// that streaming them does not push the shared pool, which every call reads again, out of the
+// last-level cache
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* base, uint32_t off) {
+    const u32x4_t v =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(base) + off));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -143,7 +153,7 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
                     const int t = min(gs + u * TPP + tl, nc - 1);  // past the chunk: a valid token, score dropped
                     const uint32_t off = (uint32_t)t * (D * 2) + (uint32_t)part * 16;
 #pragma unroll
-                    for (int c = 0; c < KL; ++c) dst[u][c] = ld16(Kc, off + c * LPT * 16);
+                    for (int c = 0; c < KL; ++c) dst[u][c] = ld16_stream(Kc, off + c * LPT * 16);
                 }
             };
             if constexpr (PF) load_k(kn, 0);
@@ -224,7 +234,7 @@ __device__ void sfx_fast_wave(const DecodeLaunch& a, int unit, float* sbuf) {
 #pragma unroll
                 for (int u = 0; u < VU; ++u) {
                     const int t = min(gs + u * TV + tv, nc - 1);  // past the chunk: a valid token, weight 0
-                    dst[u] = ld16(Vc, (uint32_t)t * (D * 2) + (uint32_t)dv * 16);
+                    dst[u] = ld16_stream(Vc, (uint32_t)t * (D * 2) + (uint32_t)dv * 16);
                 }
             };
             if constexpr (PF) load_v(vn, 0);
