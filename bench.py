@@ -140,7 +140,8 @@ def kernel_source_sha256():
 
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_shared_kv_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("pkv_decode_mfma.h", "pkv_decode_mfma.hip", "pkv_decode_mfma_split.hip"):
+    # the pool kernel's sources, with the window code its split-record form runs
+    for f in ("pkv_decode_mfma.h", "pkv_decode_mfma.hip", "pkv_decode_mfma_split.hip", "pkv_sfx.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
