@@ -1102,6 +1102,18 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // ---- fused finish: per row, inverse FWHT (H / D), suffix record, normalise, store.
     // The Hadamard butterflies run over the dimension bits: the low log2 FD in-lane, the
     // high four across the row's 16 lanes (lane distance 1, 2, 4, 8: DPP moves only)
+    // The rotation's signs of this lane's output dimensions FD fl .. FD fl + FD - 1, the same
+    // for every row: picked from the four (scalar) mask words once, rather than indexed per
+    // row, which is a vector load whose wait would also wait for the previous row's stores.
+    // (The empty asm hands the selects the words in scalar registers, so that the compiler
+    // does not fold them back into one indexed load.)
+    const uint32_t sbits = [&] {
+        const int d0 = FD * fl, w = d0 >> 5;
+        uint32_t v0 = P.vsign[0], v1 = P.vsign[1], v2 = P.vsign[2], v3 = P.vsign[3];
+        asm("" : "+s"(v0), "+s"(v1), "+s"(v2), "+s"(v3));
+        const uint32_t word = w == 0 ? v0 : w == 1 ? v1 : w == 2 ? v2 : v3;
+        return (word >> (d0 & 31)) & ((1u << FD) - 1u);
+    }();
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
         if (wave + kWaves * 4 * i >= R) break;  // no row of this pass is stored
@@ -1157,12 +1169,9 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         stage(std::integral_constant<int, 2>{});
         stage(std::integral_constant<int, 4>{});
         stage(std::integral_constant<int, 8>{});
-        {  // the rotation's signs: output dimension FD * fl + e negated where its bit is set
-            const int d0 = FD * fl;
-            const uint32_t sb = (P.vsign[d0 >> 5] >> (d0 & 31)) & ((1u << FD) - 1u);
+        // the rotation's signs: output dimension FD * fl + e negated where its bit is set
 #pragma unroll
-            for (int e = 0; e < FD; ++e) z[e] = __uint_as_float(__float_as_uint(z[e]) ^ (((sb >> e) & 1u) << 31));
-        }
+        for (int e = 0; e < FD; ++e) z[e] = __uint_as_float(__float_as_uint(z[e]) ^ (((sbits >> e) & 1u) << 31));
         const float mu = su_m[i];
         const float M2 = fmaxf(M, mu);
         const float ap = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - M2);
