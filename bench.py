@@ -340,6 +340,9 @@ def main():
     warm_achieved = alg / (avg_pool_ms / 1e3) / 1e9
     cold_avg_ms = float(np.mean(cold_ms))
     achieved = alg / (cold_avg_ms / 1e3) / 1e9
+    decode_us = (ms_per_step - float(np.mean(build_ms))) / steps_per_job * 1e3
+    window_avg = sum(sum(sfx_lens(s)) * L * Hkv * d * 2 * 2 for s in range(steps_per_job)) / steps_per_job
+    call_alg = alg + window_avg
     traffic = None
     variant = "valu" if kernel == pk.KERNEL_VALU else "mfma"  # the default selects MFMA at 60 rows
     if os.path.exists(args.traffic_json):
@@ -381,7 +384,14 @@ def main():
                                 "bytes": flush_bytes,
                                 "kernel": "pkv_stream_read (16-byte non-temporal loads, grid stride)"},
         "pool_build_us": float(np.mean(build_ms)) * 1e3,
-        "decode_step_us": (ms_per_step - float(np.mean(build_ms))) / steps_per_job * 1e3,
+        "decode_step_us": decode_us,
+        # the whole decode call: pool kernel bytes plus the agents' bf16 windows (keys and values)
+        # at the job's window lengths, averaged over its decode steps, against the call's time
+        "whole_call": {"alg_bytes_per_call": call_alg, "avg_call_us": decode_us,
+                       "achieved": call_alg / decode_us / 1e3, "unit": "GB/s",
+                       "frac": call_alg / decode_us / 1e3 / HBM_PEAK_GBPS,
+                       "window_bytes_per_call": window_avg,
+                       "note": "one all-layer call per decode step: native-window and pool kernels; build excluded"},
     }
     if per_layer is not None:
         line["per_layer"] = per_layer
