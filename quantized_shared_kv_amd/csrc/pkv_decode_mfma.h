@@ -81,8 +81,13 @@ struct Ring {
     static constexpr int kStageBytes = 32 * D + 16 * D + 256;
 };
 
+// Centroid tables of 2, 3 and 4 bits, each multiplied by its fp16 operand scale s (the LUT
+// holds fp16 (s * c), much closer to s * c than fp16 (c) is to c), with ls = log2 s, which the
+// weights' exponent takes off (w = p * Vn / s), and lsc = 2^ls, which puts the row sums back.
 struct CentArg {
     float c[3][16];
+    float ls[3];
+    float lsc[3];
 };
 
 union H8 {
@@ -135,17 +140,17 @@ __device__ __forceinline__ void touch_kernel_args() {
     constexpr int kS1 = offsetof(DecodeLaunch, sm_log2);    // last scalar field
     constexpr int kC0 = (sizeof(DecodeLaunch) + alignof(CentArg) - 1) / alignof(CentArg) * alignof(CentArg);
     constexpr int kC1 = kC0 + sizeof(CentArg) - 4;          // last word of the centroid table
-    static_assert(kPool > 128 && kPool < 192 && kS1 - kS0 > 64 && kS1 - kS0 <= 128 && kC1 - kC0 > 128 &&
-                      kC1 - kC0 < 192,
+    static_assert(kPool > 128 && kPool < 192 && kS1 - kS0 > 64 && kS1 - kS0 <= 128 && kC1 - kC0 > 192 &&
+                      kC1 - kC0 < 256,
                   "the argument lines touched");
     const __attribute__((address_space(4))) uint32_t* k =
         (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
-    constexpr int offs[11] = {0, 64, 128, kPool, kS0, kS0 + 64, kS1, kC0, kC0 + 64, kC0 + 128, kC1};
-    uint32_t x[11];
+    constexpr int offs[12] = {0, 64, 128, kPool, kS0, kS0 + 64, kS1, kC0, kC0 + 64, kC0 + 128, kC0 + 192, kC1};
+    uint32_t x[12];
 #pragma unroll
-    for (int i = 0; i < 11; ++i) x[i] = k[offs[i] / 4];
+    for (int i = 0; i < 12; ++i) x[i] = k[offs[i] / 4];
     asm volatile("" ::"s"(x[0]), "s"(x[1]), "s"(x[2]), "s"(x[3]), "s"(x[4]), "s"(x[5]), "s"(x[6]), "s"(x[7]),
-                 "s"(x[8]), "s"(x[9]), "s"(x[10]));
+                 "s"(x[8]), "s"(x[9]), "s"(x[10]), "s"(x[11]));
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
@@ -569,7 +574,10 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             }
         }
     }
-    const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x
+    const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x (times the table's s)
+    // log2 of the table's fp16 operand scale: every row reference below carries -lscale, so the
+    // weights come out divided by s (the row maxima and records do not)
+    const float lscale = cents.ls[BITS - 2];
 
     // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i).
     // Each row is first multiplied by 2^-e, e = max(0, E - 15) with max|q| < 2^E, so every
@@ -775,7 +783,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 if (t0 + 8 * lg + i < te) mx = fmaxf(mx, S[i >> 2][i & 3] * ff[i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            cref[rt] = (float)lnu - (mx + kMargin);
+            cref[rt] = (float)lnu - (mx + kMargin) - lscale;
         }
     }
 
@@ -942,7 +950,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) M = fmaxf(M, g_m[w][16 * rt + rl]);
-            cref[rt] = (float)lnu - M;
+            cref[rt] = (float)lnu - M - lscale;
         }
         lds_barrier();
     }
@@ -953,8 +961,8 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     float m[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        m[rt] = my_steps > 0 ? (float)lnu - cref[rt] : -INFINITY;
-        lsum[rt] *= inv_nu;
+        m[rt] = my_steps > 0 ? (float)lnu - (cref[rt] + lscale) : -INFINITY;
+        lsum[rt] *= inv_nu * cents.lsc[BITS - 2];
     }
 
     // ---- combine the 4 wavefronts (fixed order, so results do not depend on timing)
@@ -1249,7 +1257,12 @@ int launch_d(const DecodeLaunch& a, int wg, hipStream_t s, const CentArg& c, int
 template <bool FUSED>
 int launch_pool_mfma_form(const DecodeLaunch& a, int total_wg, hipStream_t s, int rt, bool split_q) {
     CentArg c;
-    std::memcpy(c.c, codebook_tables().cent, sizeof(c.c));
+    const CodebookTables& t = codebook_tables();
+    for (int b = 0; b < 3; ++b) {
+        for (int k = 0; k < 16; ++k) c.c[b][k] = t.fp16_scale[b] * t.cent[b][k];
+        c.ls[b] = (float)std::log2((double)t.fp16_scale[b]);
+        c.lsc[b] = (float)std::exp2((double)c.ls[b]);
+    }
     if (a.d == 128) return split_q ? launch_d<128, true, FUSED>(a, total_wg, s, c, rt) : launch_d<128, false, FUSED>(a, total_wg, s, c, rt);
     return split_q ? launch_d<64, true, FUSED>(a, total_wg, s, c, rt) : launch_d<64, false, FUSED>(a, total_wg, s, c, rt);
 }

@@ -48,6 +48,34 @@ void lloyd_positive(int bits, double* c) {
     }
 }
 
+// x rounded to the nearest fp16 value, ties to even (x a normal fp16 magnitude: 2^-14 <= |x| < 65504)
+double round_fp16(float x) {
+    int e = 0;
+    std::frexp(x, &e);  // |x| in [2^(e-1), 2^e): 11 significant bits in fp16
+    return std::ldexp(std::nearbyint(std::ldexp((double)x, 11 - e)), e - 11);
+}
+
+// The scale s of one table (see CodebookTables::fp16_scale): the positive centroids are
+// enough (the table is symmetric).
+void fp16_operand_scale(const float* cpos, int half, float* scale, float* err) {
+    double best = INFINITY;
+    float best_s = 1.0f;
+    for (int j = 0; j < (1 << 16); ++j) {
+        const float sc = 1.0f + (float)j / 65536.0f;  // exact in fp32
+        double worst = 0.0;
+        for (int k = 0; k < half && worst < best; ++k) {
+            const float v = sc * cpos[k];  // the fp32 value the device rounds to fp16
+            worst = std::fmax(worst, std::fabs(round_fp16(v) / sc - (double)cpos[k]) / (double)cpos[k]);
+        }
+        if (worst < best) {
+            best = worst;
+            best_s = sc;
+        }
+    }
+    *scale = best_s;
+    *err = (float)best;
+}
+
 CodebookTables build_tables() {
     CodebookTables t;
     std::memset(&t, 0, sizeof(t));
@@ -67,6 +95,7 @@ CodebookTables build_tables() {
             thr[half - 1 + j] = (float)m;
             thr[half - 1 - j] = (float)(-m);
         }
+        fp16_operand_scale(cent + half, half, &t.fp16_scale[bits - 2], &t.fp16_err[bits - 2]);
     }
     return t;
 }

@@ -14,6 +14,12 @@ namespace pkv {
 struct CodebookTables {
     float thr[3][15];
     float cent[3][16];
+    // fp16 operand scale of each table: fp16(fp32(s * c)) / s is within the smallest relative
+    // distance of c, over s = 1 + j / 2^16 (j < 2^16), that any s reaches for every centroid
+    // at once.  The matrix-core decode takes its centroids as fp16 (s * c) and divides s back
+    // out of the weights; fp16 (c) itself is off by up to 4.9e-4 (4 bits).
+    float fp16_scale[3];
+    float fp16_err[3];  // that largest relative distance, per table
 };
 
 // Computed once on the host from the Lloyd-Max conditions (see pkv_host.cpp).
