@@ -4,7 +4,8 @@ Each case draws its shapes from a fixed seed: layers, kv heads, query group size
 pool tokens (ragged, 1 to 700), agents (1 to 40, so up to 320 rows per kv head: several row
 blocks at the larger groups), shared or per-agent pools, uniform 3-bit or mixed 2/3/4-bit layers, the
 value recipe and dtype of one of the named workloads, and each agent's native-window
-length (0 to the capacity).  The pool image must match the oracle byte for byte and the
+length (0 to the capacity), and the codec variant (K scale per tensor, token or channel; plain
+or corrected V norm).  The pool image must match the oracle byte for byte and the
 attention outputs the fp64 oracle within 1e-3, as in the fixed cases; the sweep adds the
 combinations those do not name.
 """
@@ -46,20 +47,24 @@ def _case(i):
                      v_bits_mode="mixed" if rng.random() < 0.5 else "uniform3", seed=int(rng.integers(0, 1 << 16)))
     lens = [int(rng.integers(0, cap + 1)) for _ in range(agents)] if cap else [0] * agents
     kernel = pk.KERNEL_DEFAULT if i % 3 else pk.KERNEL_VALU
-    return w, w.n_layers, lens, distinct, kernel
+    # the codec variant: K scale per tensor (the pages'), per token or per channel; plain or
+    # corrected V norm
+    k_scale = [pk.KSCALE_TENSOR, pk.KSCALE_TOKEN, pk.KSCALE_CHANNEL][int(rng.integers(0, 3))]
+    v_norm = pk.VNORM_CORRECTED if rng.random() < 0.3 else pk.VNORM_PLAIN
+    return w, w.n_layers, lens, distinct, kernel, k_scale, v_norm
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_decode_matches_oracle(i):
     import gpu_helpers as h
 
-    w, layers, lens, distinct, kernel = _case(i)
+    w, layers, lens, distinct, kernel, k_scale, v_norm = _case(i)
     print(f"[sweep] case {i}: d={w.head_dim} dtype={w.dtype} L={layers} Hkv={w.n_kv_heads} G={w.group} "
           f"T={w.pool_tokens} A={w.n_agents} pools={w.n_pools} bits={w.v_bits_mode} lens={lens} "
-          f"kernel={kernel}", flush=True)
+          f"kernel={kernel} k_scale={k_scale} v_norm={v_norm}", flush=True)
     A = w.n_agents
     n_pools = A if distinct else 1
-    pairs = [h.build_pair(w, p, layers=layers) for p in range(n_pools)]
+    pairs = [h.build_pair(w, p, layers=layers, k_scale=k_scale, v_norm=v_norm) for p in range(n_pools)]
     for dp, ref in pairs:
         bad = h.compare_image(dp, ref)
         assert not any(bad.values()), bad
