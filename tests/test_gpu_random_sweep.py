@@ -5,7 +5,8 @@ pool tokens (ragged, 1 to 700), agents (1 to 40, so up to 320 rows per kv head: 
 blocks at the larger groups), shared or per-agent pools, uniform 3-bit or mixed 2/3/4-bit layers, the
 value recipe and dtype of one of the named workloads, and each agent's native-window
 length (0 to the capacity), and the codec variant (K scale per tensor, token or channel; plain
-or corrected V norm).  The pool image must match the oracle byte for byte and the
+or corrected V norm); odd cases decode a random layer sub-range with 2 to 8 forced token splits
+(the split-record launch and its merge).  The pool image must match the oracle byte for byte and the
 attention outputs the fp64 oracle within 1e-3, as in the fixed cases; the sweep adds the
 combinations those do not name.
 """
@@ -75,9 +76,24 @@ def test_random_decode_matches_oracle(i):
         kd, vd, ksf, vsf = h.make_suffix(w, range(A), layers)
         sfx = (kd, vd)
     pools = [pairs[a if distinct else 0][0].pool for a in range(A)]
-    out = h.run_decode(pools, q, sfx, lens, kernel=kernel)
+    # half the cases decode a layer sub-range with forced token splits (the split-record pool launch,
+    # its window workgroups and k_merge); the others every layer with the planner's choice
+    rng = np.random.default_rng(5000 + i)
+    lb, splits = 0, 0
+    if i % 2:
+        lb = int(rng.integers(0, layers))
+        splits = int(rng.integers(2, 9))
+        q = q[:, lb:].contiguous()
+        q32 = q32[:, lb:]
+        if sfx is not None:
+            sfx = (sfx[0][:, lb:].contiguous(), sfx[1][:, lb:].contiguous())
+            ksf0, vsf0 = ksf, vsf
+            ksf = lambda a, l: ksf0(a, l + lb)  # noqa: E731
+            vsf = lambda a, l: vsf0(a, l + lb)  # noqa: E731
+    print(f"[sweep] case {i}: layers {lb}..{layers - 1}, splits {splits or 'auto'}", flush=True)
+    out = h.run_decode(pools, q, sfx, lens, layer_begin=lb, kernel=kernel, splits=splits)
     ref = h.oracle_decode(q32, [a if distinct else 0 for a in range(A)], [p[1] for p in pairs], ksf, vsf,
-                          lens, w.n_kv_heads)
+                          lens, w.n_kv_heads, layer_begin=lb)
     assert out.shape == ref.shape and np.all(np.isfinite(out))
     err = attention.max_rel_error(out, ref)
     print(f"[sweep] case {i}: max relative error {err:.2e}", flush=True)
