@@ -121,6 +121,10 @@ __device__ __forceinline__ BigLds<D>& big_lds() {
 __shared__ float g_m[kWaves][64];
 __shared__ float g_l[kWaves][64];
 __shared__ int g_flag;
+// head_dim 128, fp16 query operands: each wavefront converts one 16-row tile and shares it
+__shared__ uint4 g_qst[kWaves][4][64];
+__shared__ float g_qsc[kWaves][16];
+__shared__ int g_qany[kWaves];
 
 __device__ __forceinline__ int find_pool_m(const DecodeLaunch& a, int wg) {
     int p = 0;
@@ -523,131 +527,182 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     // ---- set-up loads first, all at once: this lane's query chunks (8 values per
     // (row tile, k-step): one 16-byte load for bf16, two for fp32) and one codebook
     // entry per lane; the ring's loads follow the query conversion
-    constexpr int QV = QSPLIT ? 2 : 1;
-    // hi + lo query operands (QSPLIT) for fp32 queries, and for bf16 queries that carry a
-    // per-channel pool's K scales
-    const bool q32 = a.q_dtype == PKV_F32;
-    uint4 qraw[RT][KS][QV];
-    bool rok[RT];
-    // the rows' agents and heads first (a table lookup only when the pool's agents are not
-    // consecutive call agents), so that no wait for a lookup falls between the query loads
-    int q_agent[RT], q_head[RT];
-    const float rG = __builtin_amdgcn_rcpf((float)a.G);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int rho = 16 * rt + rl;
-        rok[rt] = rho < R;
-        const int rr = r0 + (rok[rt] ? rho : 0);        // pool row
-        const int ka = (int)(((float)rr + 0.5f) * rG);  // rr / G, exact for rows < 2^20
-        q_agent[rt] = P.agent0 + ka;
-        q_head[rt] = g * a.G + rr - ka * a.G;
-    }
-    if (P.agent_base >= 0) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) q_agent[rt] += P.agent_base - P.agent0;
-    } else {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) q_agent[rt] = a.agent_id[q_agent[rt]];
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const uint64_t qo = (((uint64_t)q_agent[rt] * a.lc + lj) * a.hq + q_head[rt]) * D + lg * DL;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            if (QSPLIT && q32) {
-                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qo + 8 * k);
-                qraw[rt][k][0] = src[0];
-                qraw[rt][k][QV - 1] = src[1];
-            } else {
-                qraw[rt][k][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + 8 * k);
-            }
-        }
-    }
-    // a per-channel pool's scales of this lane's query dimensions (lg*DL + 8 k + i), folded into q
-    float4 chs[QSPLIT ? KS : 1][2];
-    if constexpr (QSPLIT) {
-        if (kchan) {
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                chs[k][0] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k);
-                chs[k][1] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k + 4);
-            }
-        }
-    }
     const float cl = cents.c[BITS - 2][lane & 15];  // lane x holds centroid x (times the table's s)
     // log2 of the table's fp16 operand scale: every row reference below carries -lscale, so the
     // weights come out divided by s (the row maxima and records do not)
     const float lscale = cents.ls[BITS - 2];
 
-    // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i).
-    // Each row is first multiplied by 2^-e, e = max(0, E - 15) with max|q| < 2^E, so every
-    // operand is below 2^15 (fp16 holds up to 65504); the power of two is exact and the
-    // scores are multiplied back by qsc = 2^e.  bf16 values then convert exactly (8
-    // significant bits; only values more than 2^39 below the row's largest reach fp16's
-    // subnormal range), fp32 values are split into fp16 hi + lo operands.
+    // QSHARE (head_dim 128, fp16 query operands): each wavefront loads and converts one 16-row
+    // tile (wave w, tile w) into LDS, and every wavefront reads all of them after the barrier
+    constexpr bool QSHARE = !QSPLIT && D == 128;
     half8 qreg[RT][KS];  // kept in registers for the whole unit
     half8 qlo[QSPLIT ? RT : 1][QSPLIT ? KS : 1];
     float qsc[RT];
-    bool any_scaled = false;
+    bool scaled_rows = false;
+    if constexpr (QSHARE) {
+        if (wave < RT) {
+            const int rt = wave;
+            const int rho = 16 * rt + rl;
+            const bool ok = rho < R;
+            const int rr = r0 + (ok ? rho : 0);
+            const float rG = __builtin_amdgcn_rcpf((float)a.G);
+            const int ka = (int)(((float)rr + 0.5f) * rG);  // rr / G, exact for rows < 2^20
+            const int qa = P.agent_base >= 0 ? P.agent_base + ka : a.agent_id[P.agent0 + ka];
+            const int qh = g * a.G + rr - ka * a.G;
+            const uint64_t qo = (((uint64_t)qa * a.lc + lj) * a.hq + qh) * D + lg * DL;
+            uint4 qr[KS];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float xs[KS][8];
-        float mx = 0.0f;
+            for (int k = 0; k < KS; ++k)
+                qr[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + 8 * k);
+            float xs[KS][8];
+            float mx = 0.0f;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            uint32_t w[8];
-            if (QSPLIT && q32) {
-                const uint4 r0 = qraw[rt][k][0], r1 = qraw[rt][k][QV - 1];
-                w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
-                w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
-            } else {
-                const uint4 r0 = qraw[rt][k][0];
-                const uint32_t h[4] = {r0.x, r0.y, r0.z, r0.w};
+            for (int k = 0; k < KS; ++k) {
+                const uint32_t h[4] = {qr[k].x, qr[k].y, qr[k].z, qr[k].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    w[2 * i] = h[i] << 16;              // bf16 -> fp32 bits
-                    w[2 * i + 1] = h[i] & 0xffff0000u;
+                    xs[k][2 * i] = ok ? __uint_as_float(h[i] << 16) : 0.0f;
+                    xs[k][2 * i + 1] = ok ? __uint_as_float(h[i] & 0xffff0000u) : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(xs[k][i]));
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            int ex = 0;
+            frexpf(mx, &ex);  // mx < 2^ex
+            const int e = ex > 15 ? ex - 15 : 0;
+            const float qinv = ldexpf(1.0f, -e);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                H8 hv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv.u[i] = pack_h2(xs[k][2 * i] * qinv, xs[k][2 * i + 1] * qinv);
+                g_qst[rt][k][lane] = hv.v;
+            }
+            if (lg == 0) g_qsc[rt][rl] = ldexpf(1.0f, e);
+            const bool any = __builtin_amdgcn_ballot_w64(e > 0) != 0ull;
+            if (lane == 0) g_qany[rt] = any ? 1 : 0;
+        }
+    } else {
+        constexpr int QV = QSPLIT ? 2 : 1;
+        // hi + lo query operands (QSPLIT) for fp32 queries, and for bf16 queries that carry a
+        // per-channel pool's K scales
+        const bool q32 = a.q_dtype == PKV_F32;
+        uint4 qraw[RT][KS][QV];
+        bool rok[RT];
+        // the rows' agents and heads first (a table lookup only when the pool's agents are not
+        // consecutive call agents), so that no wait for a lookup falls between the query loads
+        int q_agent[RT], q_head[RT];
+        const float rG = __builtin_amdgcn_rcpf((float)a.G);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rho = 16 * rt + rl;
+            rok[rt] = rho < R;
+            const int rr = r0 + (rok[rt] ? rho : 0);        // pool row
+            const int ka = (int)(((float)rr + 0.5f) * rG);  // rr / G, exact for rows < 2^20
+            q_agent[rt] = P.agent0 + ka;
+            q_head[rt] = g * a.G + rr - ka * a.G;
+        }
+        if (P.agent_base >= 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) q_agent[rt] += P.agent_base - P.agent0;
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) q_agent[rt] = a.agent_id[q_agent[rt]];
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint64_t qo = (((uint64_t)q_agent[rt] * a.lc + lj) * a.hq + q_head[rt]) * D + lg * DL;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                if (QSPLIT && q32) {
+                    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qo + 8 * k);
+                    qraw[rt][k][0] = src[0];
+                    qraw[rt][k][QV - 1] = src[1];
+                } else {
+                    qraw[rt][k][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qo + 8 * k);
                 }
             }
+        }
+        // a per-channel pool's scales of this lane's query dimensions (lg*DL + 8 k + i), folded into q
+        float4 chs[QSPLIT ? KS : 1][2];
+        if constexpr (QSPLIT) {
+            if (kchan) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                xs[k][i] = rok[rt] ? __uint_as_float(w[i]) : 0.0f;
-                if constexpr (QSPLIT) {
-                    if (kchan) {  // q'_i = q_i * s_i (fp32), split into fp16 hi + lo below
-                        const float4 c = chs[k][i >> 2];
-                        xs[k][i] *= (i & 3) == 0 ? c.x : (i & 3) == 1 ? c.y : (i & 3) == 2 ? c.z : c.w;
+                for (int k = 0; k < KS; ++k) {
+                    chs[k][0] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k);
+                    chs[k][1] = *reinterpret_cast<const float4*>(kch + lg * DL + 8 * k + 4);
+                }
+            }
+        }
+        // queries -> fp16 B operands (lane (lg, rl): row 16 rt + rl, dims lg*DL + 8 k + i).
+        // Each row is first multiplied by 2^-e, e = max(0, E - 15) with max|q| < 2^E, so every
+        // operand is below 2^15 (fp16 holds up to 65504); the power of two is exact and the
+        // scores are multiplied back by qsc = 2^e.  bf16 values then convert exactly (8
+        // significant bits; only values more than 2^39 below the row's largest reach fp16's
+        // subnormal range), fp32 values are split into fp16 hi + lo operands.
+        bool any_scaled = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float xs[KS][8];
+            float mx = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                uint32_t w[8];
+                if (QSPLIT && q32) {
+                    const uint4 r0 = qraw[rt][k][0], r1 = qraw[rt][k][QV - 1];
+                    w[0] = r0.x; w[1] = r0.y; w[2] = r0.z; w[3] = r0.w;
+                    w[4] = r1.x; w[5] = r1.y; w[6] = r1.z; w[7] = r1.w;
+                } else {
+                    const uint4 r0 = qraw[rt][k][0];
+                    const uint32_t h[4] = {r0.x, r0.y, r0.z, r0.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        w[2 * i] = h[i] << 16;              // bf16 -> fp32 bits
+                        w[2 * i + 1] = h[i] & 0xffff0000u;
                     }
                 }
-                mx = fmaxf(mx, fabsf(xs[k][i]));
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        int ex = 0;
-        frexpf(mx, &ex);  // mx < 2^ex
-        const int e = ex > 15 ? ex - 15 : 0;
-        qsc[rt] = ldexpf(1.0f, e);
-        const float qinv = ldexpf(1.0f, -e);
-        any_scaled |= e > 0;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            H8 hv, lv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x0 = xs[k][2 * i] * qinv, x1 = xs[k][2 * i + 1] * qinv;
-                hv.u[i] = pack_h2(x0, x1);
-                if constexpr (QSPLIT) {
-                    const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
-                    lv.u[i] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                for (int i = 0; i < 8; ++i) {
+                    xs[k][i] = rok[rt] ? __uint_as_float(w[i]) : 0.0f;
+                    if constexpr (QSPLIT) {
+                        if (kchan) {  // q'_i = q_i * s_i (fp32), split into fp16 hi + lo below
+                            const float4 c = chs[k][i >> 2];
+                            xs[k][i] *= (i & 3) == 0 ? c.x : (i & 3) == 1 ? c.y : (i & 3) == 2 ? c.z : c.w;
+                        }
+                    }
+                    mx = fmaxf(mx, fabsf(xs[k][i]));
                 }
             }
-            qreg[rt][k] = hv.h;
-            asm volatile("" : "+a"(qreg[rt][k]));  // a matrix-core operand only: kept in AGPRs
-            if constexpr (QSPLIT) qlo[rt][k] = lv.h;
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            int ex = 0;
+            frexpf(mx, &ex);  // mx < 2^ex
+            const int e = ex > 15 ? ex - 15 : 0;
+            qsc[rt] = ldexpf(1.0f, e);
+            const float qinv = ldexpf(1.0f, -e);
+            any_scaled |= e > 0;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                H8 hv, lv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = xs[k][2 * i] * qinv, x1 = xs[k][2 * i + 1] * qinv;
+                    hv.u[i] = pack_h2(x0, x1);
+                    if constexpr (QSPLIT) {
+                        const half2v hh = __builtin_bit_cast(half2v, hv.u[i]);
+                        lv.u[i] = pack_h2(x0 - (float)hh[0], x1 - (float)hh[1]);
+                    }
+                }
+                qreg[rt][k] = hv.h;
+                asm volatile("" : "+a"(qreg[rt][k]));  // a matrix-core operand only: kept in AGPRs
+                if constexpr (QSPLIT) qlo[rt][k] = lv.h;
+            }
         }
+        // every wavefront of the workgroup holds all rows, so they all take the same branch below
+        scaled_rows = __builtin_amdgcn_ballot_w64(any_scaled) != 0ull;
     }
-    // every wavefront of the workgroup holds all rows, so they all take the same branch below
-    const bool scaled_rows = __builtin_amdgcn_ballot_w64(any_scaled) != 0ull;
     // the ring's first steps: issued once the query loads have landed, so those do not queue
     // behind the ring's burst of loads
 #pragma unroll
@@ -685,6 +740,20 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
         }
     }
     lds_barrier();  // LUT and query operands ready
+    if constexpr (QSHARE) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                H8 h;
+                h.v = g_qst[rt][k][lane];
+                qreg[rt][k] = h.h;
+                asm volatile("" : "+a"(qreg[rt][k]));  // a matrix-core operand only: kept in AGPRs
+            }
+            qsc[rt] = g_qsc[rt][rl];
+            scaled_rows = scaled_rows || g_qany[rt] != 0;
+        }
+    }
 
     // this lane's LUT copy (pairs of 4-bit codes, quads of 2-bit ones), or the single 3-bit quad table
     const uint32_t lut_lane = lds_addr(g_big.loop.lut) +
