@@ -126,6 +126,26 @@ __shared__ uint4 g_qst[kWaves][4][64];
 __shared__ float g_qsc[kWaves][16];
 __shared__ int g_qany[kWaves];
 
+// Accumulator tiles in LDS: lane x of a 16-lane group owns F floats of a row from F x on, in
+// 16-byte slots.  Lanes x and x + 8 fall 128 floats apart, in the same banks, so from lane 8
+// on a lane's slots are taken in swapped order (slot e4 at e4 ^ 4 when F = 8): the lanes of
+// one access then cover all the banks.  Writers and readers use the same map.
+template <int F>
+__device__ __forceinline__ int acc_slot(int x, int e4) {
+    return e4 ^ (4 * ((x >> 3) & (F / 4 - 1)));
+}
+
+// x summed over lanes l, l ^ 16, l ^ 32, l ^ 48 (the wavefront's four 16-lane rows), as
+// (x_l + x_(l^16)) + (x_(l^32) + x_(l^48)) in every lane.  The lane index is computed here
+// (and hidden from common-subexpression elimination), so no copy of it from the kernel's
+// start stays live, or spilled, across the token loop.
+__device__ __forceinline__ float sum_lane_rows(float x) {
+    int lid;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+    x += __int_as_float(__builtin_amdgcn_ds_bpermute((lid ^ 16) << 2, __float_as_int(x)));
+    return x + __int_as_float(__builtin_amdgcn_ds_bpermute((lid ^ 32) << 2, __float_as_int(x)));
+}
+
 __device__ __forceinline__ int find_pool_m(const DecodeLaunch& a, int wg) {
     int p = 0;
     while (p + 1 < a.n_pools && wg >= a.pools[p + 1].wg_begin) ++p;
@@ -474,7 +494,10 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     frexpf(vmax, &ex);
     // vn * nu < 2^7, so w = p * vn * nu < 2^15 fits fp16 while keeping the lo part of
     // small weights out of the fp16 subnormal range
-    const int lnu = (vmax > 0.0f ? -ex : 0) + kWeightExp;
+    const int lnu0 = (vmax > 0.0f ? -ex : 0) + kWeightExp;
+    // wave-uniform: the fused form holds it in a scalar register, so its combine needs no spilled
+    // copy of it (the split form's code is different enough to keep it as it is)
+    const int lnu = FUSED ? __builtin_amdgcn_readfirstlane(lnu0) : lnu0;
     const float nu = ldexpf(1.0f, lnu);
 
     const int tb = sp * P.chunk;
@@ -1107,8 +1130,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        lsum[rt] += __shfl_xor(lsum[rt], 16, 64);
-        lsum[rt] += __shfl_xor(lsum[rt], 32, 64);
+        lsum[rt] = sum_lane_rows(lsum[rt]);
         if (lg == 0) {
             g_m[wave][16 * rt + rl] = m[rt];
             g_l[wave][16 * rt + rl] = lsum[rt];
@@ -1124,7 +1146,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             float* dst = mine + (16 * rt + 4 * lg + j) * D + NB * rl;
 #pragma unroll
             for (int h = 0; h < NB / 4; ++h)
-                *reinterpret_cast<float4*>(dst + 4 * h) =
+                *reinterpret_cast<float4*>(dst + acc_slot<NB>(rl, 4 * h)) =
                     make_float4(acc[rt][4 * h][j], acc[rt][4 * h + 1][j], acc[rt][4 * h + 2][j], acc[rt][4 * h + 3][j]);
         }
     lds_barrier();
@@ -1161,7 +1183,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
                 const float* src = g_big.accs + w * (kMaxRows * D) + row * D + FD * fl;
 #pragma unroll
                 for (int e4 = 0; e4 < FD; e4 += 4) {
-                    const float4 v = *reinterpret_cast<const float4*>(src + e4);
+                    const float4 v = *reinterpret_cast<const float4*>(src + acc_slot<FD>(fl, e4));
                     z[e4] = fmaf(al[w], v.x, z[e4]);
                     z[e4 + 1] = fmaf(al[w], v.y, z[e4 + 1]);
                     z[e4 + 2] = fmaf(al[w], v.z, z[e4 + 2]);
@@ -1205,7 +1227,7 @@ __device__ __forceinline__ void pool_mfma_body(const DecodeLaunch& a, const Cent
             const float* src = g_big.accs + w * (kMaxRows * D) + row * D + FD * fl;
 #pragma unroll
             for (int e4 = 0; e4 < FD; e4 += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(src + e4);
+                const float4 v = *reinterpret_cast<const float4*>(src + acc_slot<FD>(fl, e4));
                 z[e4] = fmaf(al[w], v.x, z[e4]);
                 z[e4 + 1] = fmaf(al[w], v.y, z[e4 + 1]);
                 z[e4 + 2] = fmaf(al[w], v.z, z[e4 + 2]);
